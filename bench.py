@@ -1,0 +1,247 @@
+"""Throughput of causal GQA flash-attention prefill against a cached prefix on
+one MI355X.
+
+One step = one attn_prefill call (the whole hot path: Q load, K/V tile
+staging, scores, causal mask, online softmax, PV, normalisation, store) over
+one chunk whose inputs are already resident in HBM.
+
+Default workload: fp32 chunk C=2048 at prefix P=2048 (4096 cache positions),
+32 query heads, 8 KV heads, d=64, q/k/v i.i.d. N(0,1), synthetic and seeded.
+Metric: causal attention TFLOP/s = 4*d FLOPs per visible (row, key) pair per
+query head, divided by the time per call.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  The oracle (CPU, double) is timed on the host cores on
+the whole workload as the cpu_baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal attn TFLOP/s and % MFMA peak at C=2048,P=2048 (32q/8kv heads, d=64)"
+# MI355X dense matrix peaks (TFLOP/s): fp32 MFMA 157.3, bf16 2516.6 (no sparsity).
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (C, P, dtype, seed base, description)
+    "c2048_p2048_f32": (2048, 2048, "f32", 200,
+                        "fp32 serving chunk C=2048 at P=2048 (4096 KV positions), 32 query heads, 8 KV heads, "
+                        "d=64, q/k/v i.i.d. N(0,1)"),
+    "c512_p15872_f32": (512, 15872, "f32", 400,
+                        "fp32 long cached prefix C=512 at P=15872 (16384 KV positions), last key of KV head 0 "
+                        "planted at 4.0"),
+    "t2048_p0_f32": (2048, 0, "f32", 300, "fp32 plain causal prompt prefill T=2048, P=0"),
+    "c4096_p28672_bf16": (4096, 28672, "bf16", 500,
+                          "bf16 q/k/v, fp32 accumulation and output, C=4096 at P=28672 (32768 KV positions)"),
+}
+DEFAULT = "c2048_p2048_f32"
+KERNEL_NAME = "attn_prefill_kernel"
+KERNEL_SRC = os.path.join(ROOT, "chunked_prefill_flash_amd", "csrc", "attn_prefill.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def make_inputs(name):
+    import synth
+    C, P, dt, seed, _ = WORKLOADS[name]
+    if name.startswith("c512_p15872"):
+        q, k, v, _ = synth.case_last_key(C, P, seed)
+    else:
+        q, k, v = synth.case_plain(C, P, seed)
+    return q, k, v
+
+
+def to_device(x, dt, dev):
+    import numpy as np
+    import torch
+    import synth
+    if dt == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    return torch.from_numpy(synth.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def traffic_entry(name):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs, scaled by the copy-kernel calibration; None when missing or taken
+    on a different kernel source."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = data.get(name)
+    if not e or e.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(name, q, k, v, P, dt, budget_s=12.0):
+    """Time the CPU oracle, on all the host threads OpenMP gives it.
+
+    The whole workload is run when a short trial predicts it fits the budget
+    (repeated up to 3 times while it does); otherwise an evenly spaced sample
+    of rows (all 32 heads each) sized to the budget.  The value counts the
+    same 4*d FLOPs per visible pair as the GPU figure, over what was run."""
+    import numpy as np
+    import oracle
+    import synth
+    import chunked_prefill_flash_amd as cpf
+    if dt == "bf16":
+        q, k, v = (synth.bf16_bits_to_f32(synth.to_bf16_bits(x)) for x in (q, k, v))
+    C = q.shape[0]
+    threads = oracle.max_threads()
+
+    def rows_flop(rows):
+        return int(sum(4 * 64 * 32 * (P + int(r) + 1) for r in rows))
+
+    def run_rows(rows):
+        rr = np.repeat(np.asarray(rows), 32)
+        hh = np.tile(np.arange(32), len(rows))
+        t0 = time.perf_counter()
+        oracle.attn_rows(q, k, v, P, rr, hh)
+        return time.perf_counter() - t0
+
+    trial = np.linspace(0, C - 1, num=min(C, 16)).astype(int)
+    rate = rows_flop(trial) / run_rows(trial)            # FLOP/s of the oracle
+    full = cpf.flops(C, P)
+    if full / rate <= budget_s:
+        times = []
+        t_all = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            oracle.attn_prefill(q, k, v, P)
+            times.append(time.perf_counter() - t0)
+            if len(times) >= 3 or time.perf_counter() - t_all + times[-1] > budget_s:
+                break
+        per = float(np.mean(times))
+        return {"value": round(full / per / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": "whole workload (all %d rows x 32 heads), %d run(s), mean %.3f s per run, double "
+                          "sums, OpenMP over (row, head)" % (C, len(times), per)}
+    n = int(max(16, min(C, C * budget_s * rate / full)))
+    rows = np.linspace(0, C - 1, num=n).astype(int)
+    t = run_rows(rows)
+    return {"value": round(rows_flop(rows) / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d evenly spaced rows of %d (all 32 heads each, %.3g GFLOP), %.2f s, double sums, "
+                      "OpenMP over (row, head)" % (n, C, rows_flop(rows) / 1e9, t)}
+
+
+def sampled_parity(got, q, k, v, P, dt):
+    """Spot-check the benchmarked output against the oracle on 8 rows."""
+    import numpy as np
+    import oracle
+    import synth
+    C = q.shape[0]
+    if dt == "bf16":
+        q, k, v = (synth.bf16_bits_to_f32(synth.to_bf16_bits(x)) for x in (q, k, v))
+    rows = np.array(sorted({0, 1, C // 3, C // 2, C - 2, C - 1, 7 % C, (5 * C) // 7}))
+    rr = np.repeat(rows, 32)
+    hh = np.tile(np.arange(32), len(rows))
+    ref = oracle.attn_rows(q, k, v, P, rr, hh).astype(np.float64)
+    g = got[rr, hh].astype(np.float64)
+    if dt == "f32":
+        tol = 1e-4 + 1e-3 * np.abs(ref)
+    else:
+        tol = 1e-5 + 2.0 ** -8 * oracle.attn_rows(q, k, np.abs(v), P, rr, hh).astype(np.float64)
+    err = np.abs(g - ref)
+    return bool(np.all(err <= tol)), float(err.max())
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import chunked_prefill_flash_amd as cpf
+
+    name = args.workload
+    C, P, dt, _, desc = WORKLOADS[name]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q, k, v = make_inputs(name)
+    qd, kd, vd = to_device(q, dt, dev), to_device(k, dt, dev), to_device(v, dt, dev)
+    out = torch.empty((C, 32, 64), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(max(args.warmup, 1)):
+        cpf.attn_prefill(qd, kd, vd, out=out, P=P, stream=stream)
+    torch.cuda.synchronize()
+    ok, maxerr = (True, None) if args.no_check else sampled_parity(out.cpu().numpy(), q, k, v, P, dt)
+    if not ok:
+        print("bench: sampled parity check FAILED (max err %g)" % maxerr, file=sys.stderr)
+        sys.exit(1)
+
+    # timed region: K steps, synchronised on both sides; HIP events on the
+    # stream the kernel is launched on give the per-launch device time
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        cpf.attn_prefill(qd, kd, vd, out=out, P=P, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    flop = cpf.flops(C, P)
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dt]
+    plan = cpf.plan(C, P, torch.float32 if dt == "f32" else torch.bfloat16)
+
+    result = {
+        "metric": METRIC if name == DEFAULT else "causal attn TFLOP/s (%s)" % name,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded N(0,1), inputs resident in HBM)",
+        "config": {"workload": desc, "C": C, "P": P, "q_heads": 32, "kv_heads": 8, "head_dim": 64,
+                   "flop_per_call": flop, "launch": plan},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic_entry(name),
+                     "kernel": KERNEL_NAME, "kernel_ms": round(kernel_ms, 5)},
+        "parity": {"sampled_rows_ok": ok, "max_abs_err": maxerr},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(name, q, k, v, P, dt)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+"""Causal grouped-query flash-attention prefill against a cached prefix, for
+AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of libattn_prefill.so (declared in
+include/attn_prefill.h).  This module only checks and marshals arguments: it
+passes device pointers, sizes and the current HIP stream to the library, and
+every step of the computation runs in the library's HIP kernels.  PyTorch is
+used for device memory and streams only.
+
+The operation ("Inference Attention 2: Flash Prefill Against a Cached Prefix",
+Lesson): q[C][32][64] holds a chunk of C query tokens at positions P..P+C-1;
+kCache and vCache [P+C][8][64] hold every visible position; out[C][32][64]
+(float32) receives causal attention with query head h reading KV head h/4 and
+scale 1/8.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported first so the library binds to torch's HIP runtime
+
+__all__ = ["attn_prefill", "validate", "plan", "status_string", "library_path", "load_library",
+           "flops", "visible_pairs", "AttnError", "EXPORTED_SYMBOLS", "HQ", "HKV", "D"]
+
+HQ, HKV, D = 32, 8, 64
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libattn_prefill.so")
+_lib = None
+
+# Every function include/attn_prefill.h declares.
+EXPORTED_SYMBOLS = ("attn_prefill", "attn_status_string", "attn_prefill_validate", "attn_prefill_plan",
+                    "attn_prefill_version")
+
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_NULL_PTR", 3: "ATTN_ERR_UNSUPPORTED_DTYPE",
+          4: "ATTN_ERR_MISALIGNED", 5: "ATTN_ERR_LAUNCH", 6: "ATTN_ERR_ALIAS"}
+
+
+class AttnError(RuntimeError):
+    """A nonzero attn_status_t from the library."""
+
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s returned %s (%d)" % (where, STATUS.get(code, "?"), code))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libattn_prefill.so (built by __graft_entry__.build() or
+    `python -m chunked_prefill_flash_amd.build`).  Raises if it is missing:
+    there is no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libattn_prefill.so is not built (%s); run "
+                           "`python -m chunked_prefill_flash_amd.build`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, vp]
+    lib.attn_prefill.restype = i
+    lib.attn_prefill_validate.argtypes = [vp, vp, vp, vp, i, i, i]
+    lib.attn_prefill_validate.restype = i
+    lib.attn_prefill_plan.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_int)]
+    lib.attn_prefill_plan.restype = i
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_prefill_version.argtypes = []
+    lib.attn_prefill_version.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().attn_status_string(int(code)).decode()
+
+
+def validate(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, C: int, P: int, dtype_code: int) -> int:
+    """Raw argument check of the C ABI (no GPU work); returns the status code."""
+    return int(load_library().attn_prefill_validate(q_ptr, k_ptr, v_ptr, out_ptr, C, P, dtype_code))
+
+
+def plan(C: int, P: int, dtype=torch.float32) -> dict:
+    """The launch decomposition the library uses for (C, P, dtype)."""
+    code = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    arr = (ctypes.c_int * 8)()
+    st = load_library().attn_prefill_plan(C, P, code, arr)
+    if st != 0:
+        raise AttnError(st, "attn_prefill_plan")
+    keys = ("rows_per_item", "key_splits", "grid", "threads", "items_per_workgroup", "keys_per_tile",
+            "lds_bytes", "variant")
+    return dict(zip(keys, list(arr)))
+
+
+def visible_pairs(C: int, P: int) -> int:
+    """(query row, key) pairs inside the causal edge, per query head."""
+    return C * P + C * (C + 1) // 2
+
+
+def flops(C: int, P: int) -> int:
+    """Attention FLOPs of one call: 4*d per visible pair per query head."""
+    return 4 * D * HQ * visible_pairs(C, P)
+
+
+def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
+                 P: int | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """out[C][32][64] = causal GQA attention of q against the cache (k, v).
+
+    q [C][32][64], k and v [P+C][8][64], all float32 or all bfloat16, contiguous,
+    on one GPU.  out is float32 [C][32][64] (allocated if None).  P defaults to
+    k.shape[0] - C.  Runs asynchronously on `stream` (default: current stream).
+    """
+    if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype in %s" % list(DTYPES))
+    if q.dim() != 3 or q.shape[1:] != (HQ, D):
+        raise ValueError("q must be [C][32][64], got %s" % tuple(q.shape))
+    C = q.shape[0]
+    if P is None:
+        P = k.shape[0] - C
+    if k.shape != (P + C, HKV, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [P+C][8][64] = [%d][8][64], got %s and %s"
+                         % (P + C, tuple(k.shape), tuple(v.shape)))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if out is None:
+        out = torch.empty((C, HQ, D), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.shape != (C, HQ, D) or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous float32 GPU tensor [C][32][64]")
+    if len({q.device, k.device, v.device, out.device}) != 1:
+        raise ValueError("all tensors must be on one device")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), C, P, DTYPES[q.dtype],
+                              s.cuda_stream)
+    if st != 0:
+        raise AttnError(st, "attn_prefill")
+    return out

@@ -1,0 +1,120 @@
+/*
+ * attn_prefill.h -- C ABI of the causal grouped-query flash-attention prefill
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Inference Attention 2: Flash Prefill Against a Cached
+ * Prefix", Lesson): a chunk of C new query tokens at absolute positions
+ * P .. P+C-1 attends causally to a key/value cache holding positions
+ * 0 .. P+C-1, so chunk row i sees cache positions j <= P + i.  There are 32
+ * query heads and 8 key/value heads of size 64; query head h reads KV head
+ * h / 4; the score scale is exactly 1/8.  For every row i, head h (g = h/4)
+ * and dim d:
+ *
+ *     s_j          = (1/8) * sum_k q[i][h][k] * kCache[j][g][k],  j <= P + i
+ *     out[i][h][d] = sum_j softmax_j(s)_j * vCache[j][g][d]
+ *
+ * computed in one pass over key/value tiles with an online softmax (running
+ * maximum, running denominator, accumulator rescaled when the maximum moves,
+ * one division at the end), with no score matrix and no workspace ("Inference
+ * Attention 2", Lesson, the four update equations; "FlashAttention and
+ * inference kernels", section "FlashAttention: tiling plus online softmax").
+ *
+ * Layout (all dense, row-major, no padding, element offsets fit in 64 bits):
+ *     q      [C][32][64]      dtype         (token-major, then head, then dim)
+ *     kCache [P+C][8][64]     dtype
+ *     vCache [P+C][8][64]     dtype
+ *     out    [C][32][64]      float32 for every dtype
+ *
+ * Ownership: every pointer is device memory owned by the caller.  The library
+ * allocates nothing, keeps no state between calls, and may be called from any
+ * host thread.  Work is enqueued on `stream` and the call returns without
+ * waiting; the caller synchronises.  `out` must not overlap the inputs; every
+ * element of out[0..C) is overwritten.
+ *
+ * Errors: nothing is thrown across the ABI; each call returns an
+ * attn_status_t and enqueues no work unless it returns ATTN_OK.
+ */
+#ifndef ATTN_PREFILL_H
+#define ATTN_PREFILL_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fixed shape of the tensor contract ("Inference Attention 2", Lesson). */
+#define ATTN_NUM_Q_HEADS 32
+#define ATTN_NUM_KV_HEADS 8
+#define ATTN_HEAD_DIM 64
+
+/* Element type of q, kCache and vCache.  out is always float32. */
+typedef enum {
+    ATTN_DTYPE_F32 = 0,  /* IEEE binary32; scores and PV products in fp32 MFMA */
+    ATTN_DTYPE_BF16 = 1  /* bfloat16; bf16 MFMA with fp32 accumulation, fp32 softmax state */
+} attn_dtype_t;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,      /* C < 0, P < 0, or P + C overflows int */
+    ATTN_ERR_NULL_PTR = 2,         /* a tensor pointer is NULL while C > 0 */
+    ATTN_ERR_UNSUPPORTED_DTYPE = 3,/* dtype is not an attn_dtype_t value */
+    ATTN_ERR_MISALIGNED = 4,       /* a tensor pointer is not 16-byte aligned */
+    ATTN_ERR_LAUNCH = 5,           /* the HIP runtime rejected the launch */
+    ATTN_ERR_ALIAS = 6             /* out overlaps q, kCache or vCache */
+} attn_status_t;
+
+/*
+ * attn_prefill -- out = causal GQA attention of the chunk q against the cache.
+ *
+ *   q       device pointer, [C][32][64] of dtype, 16-byte aligned
+ *   kCache  device pointer, [P+C][8][64] of dtype, 16-byte aligned
+ *   vCache  device pointer, [P+C][8][64] of dtype, 16-byte aligned
+ *   out     device pointer, [C][32][64] float32, 16-byte aligned, written
+ *   C       chunk length (number of query rows), C >= 0; C == 0 is a no-op
+ *   P       prefix length already in the cache, P >= 0
+ *   dtype   element type of q, kCache, vCache
+ *   stream  HIP stream to enqueue on (0 = the null stream)
+ *
+ * Returns ATTN_OK once the kernel is enqueued, or an error code (see
+ * attn_status_t) with nothing enqueued.  Asynchronous: errors raised while
+ * the kernel runs surface at the caller's next synchronisation.
+ */
+attn_status_t attn_prefill(const void* q, const void* kCache, const void* vCache, float* out,
+                           int C, int P, attn_dtype_t dtype, hipStream_t stream);
+
+/* Static, NUL-terminated name of a status code ("ATTN_OK", ...). */
+const char* attn_status_string(attn_status_t status);
+
+/*
+ * attn_prefill_validate -- the argument checks of attn_prefill alone, with no
+ * HIP call and no launch.  Same arguments and return codes; ATTN_OK means
+ * attn_prefill would try to launch.  Host-only; safe without a GPU.
+ */
+attn_status_t attn_prefill_validate(const void* q, const void* kCache, const void* vCache,
+                                    const float* out, int C, int P, attn_dtype_t dtype);
+
+/*
+ * attn_prefill_plan -- the launch decomposition attn_prefill would use for
+ * (C, P, dtype), written to the caller's int array plan[8]:
+ *   plan[0] rows per work item (query rows of one KV group per item)
+ *   plan[1] waves splitting the key range inside a workgroup
+ *   plan[2] workgroups in the grid
+ *   plan[3] threads per workgroup
+ *   plan[4] work items per workgroup (1, or 2 when rows are paired)
+ *   plan[5] keys per staged K/V tile
+ *   plan[6] LDS bytes per workgroup
+ *   plan[7] kernel variant id
+ * Host-only, no HIP call.  Returns ATTN_OK or ATTN_ERR_INVALID_ARG /
+ * ATTN_ERR_UNSUPPORTED_DTYPE / ATTN_ERR_NULL_PTR (plan == NULL).
+ */
+attn_status_t attn_prefill_plan(int C, int P, attn_dtype_t dtype, int* plan);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int attn_prefill_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_PREFILL_H */

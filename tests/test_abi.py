@@ -1,0 +1,157 @@
+"""The C-ABI library loads and exports every function include/*.h declares;
+argument validation and the launch plan behave as documented.  Nothing here
+touches a GPU: only host-side entry points are called."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import chunked_prefill_flash_amd as cpf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INVALID, NULLP, DTYPE, MISAL, LAUNCH, ALIAS = range(7)
+F32, BF16 = 0, 1
+A = 0x10000000          # fake, 16-byte aligned addresses: never dereferenced
+MB = 1 << 20
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cpf.library_path()):
+        pytest.fail("library not built: run `python -m chunked_prefill_flash_amd.build`")
+    return cpf.load_library()
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == set(cpf.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", cpf.library_path()], capture_output=True, text=True)
+    exported = {ln.split()[-1] for ln in out.stdout.splitlines() if ln.strip()}
+    assert declared_functions() <= exported
+
+
+def test_library_contains_gfx950_code():
+    blob = open(cpf.library_path(), "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_version(lib):
+    assert lib.attn_prefill_version() >= 100
+
+
+def test_status_strings(lib):
+    for code, name in cpf.STATUS.items():
+        assert cpf.status_string(code) == name
+    assert cpf.status_string(99) == "ATTN_ERR_UNKNOWN"
+
+
+def v(q=A, k=A + 64 * MB, vv=A + 128 * MB, out=A + 192 * MB, C=17, P=31, dt=F32):
+    return cpf.validate(q, k, vv, out, C, P, dt)
+
+
+def test_validate_accepts_good_arguments():
+    assert v() == OK
+    assert v(dt=BF16) == OK
+    assert v(C=1, P=0) == OK
+
+
+def test_validate_codes():
+    assert v(dt=2) == DTYPE
+    assert v(dt=-1) == DTYPE
+    assert v(C=-1) == INVALID
+    assert v(P=-1) == INVALID
+    assert v(C=2 ** 31 - 10, P=100) == INVALID          # P + C overflows int
+    assert v(q=0) == NULLP
+    assert v(k=0) == NULLP
+    assert v(vv=0) == NULLP
+    assert v(out=0) == NULLP
+    assert v(q=A + 4) == MISAL
+    assert v(out=A + 192 * MB + 8) == MISAL
+    assert v(k=A + 64 * MB + 2, dt=BF16) == MISAL
+
+
+def test_validate_zero_chunk_is_noop_even_without_pointers():
+    assert v(q=0, k=0, vv=0, out=0, C=0, P=5) == OK
+
+
+def test_validate_alias():
+    # out overlapping q, k or v is rejected; adjacent buffers are fine
+    C, P = 17, 31
+    qbytes = C * 32 * 64 * 4
+    assert v(out=A, q=A) == ALIAS
+    assert v(out=A + qbytes - 16, q=A) == ALIAS
+    assert v(out=A + qbytes, q=A) == OK
+    assert v(out=A + 64 * MB + 1024, k=A + 64 * MB) == ALIAS
+    assert v(out=A + 128 * MB, vv=A + 128 * MB) == ALIAS
+
+
+def test_plan_shapes():
+    p = cpf.plan(2048, 2048)
+    assert p["threads"] == 64 * (p["rows_per_item"] // 8) * p["key_splits"]
+    assert p["grid"] % 8 == 0
+    # every row tile of every KV group is covered exactly once
+    tiles = -(-2048 // p["rows_per_item"])
+    assert p["grid"] // 8 * p["items_per_workgroup"] >= tiles
+    assert p["lds_bytes"] <= 160 * 1024
+    for C in (1, 17, 33, 255, 256, 511, 512, 1023, 1024, 2047, 2048, 4096, 65536):
+        for dt in (torch_f32(), torch_bf16()):
+            pp = cpf.plan(C, 100, dt)
+            t = -(-C // pp["rows_per_item"])
+            per = pp["items_per_workgroup"]
+            assert pp["grid"] == 8 * (-(-t // per) if per == 2 else t)
+            assert pp["lds_bytes"] <= 160 * 1024
+    assert cpf.plan(0, 5)["grid"] == 0
+
+
+def test_plan_errors():
+    with pytest.raises(cpf.AttnError):
+        cpf.plan(-1, 0)
+    with pytest.raises(cpf.AttnError):
+        cpf.plan(1, 0, 7)
+
+
+def torch_f32():
+    import torch
+    return torch.float32
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16
+
+
+def test_flop_count():
+    # 4*d FLOPs per visible (row, key) pair per query head
+    assert cpf.visible_pairs(1, 0) == 1
+    assert cpf.visible_pairs(2048, 2048) == 2048 * 2048 + 2048 * 2049 // 2
+    assert cpf.flops(2048, 2048) == 8192 * 6_292_480 == 51_547_996_160
+
+
+def test_binding_rejects_bad_tensors_without_gpu():
+    import torch
+    q = torch.zeros(3, 32, 64)
+    k = torch.zeros(5, 8, 64)
+    with pytest.raises(ValueError):      # CPU tensors are refused before any library call
+        cpf.attn_prefill(q, k, k)
+    with pytest.raises(TypeError):
+        cpf.attn_prefill(q.double(), k.double(), k.double())
+    with pytest.raises(ValueError):
+        cpf.attn_prefill(q, torch.zeros(4, 8, 64), torch.zeros(4, 8, 64), P=2)

@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Tolerances ("Inference Attention 2: Flash Prefill Against a Cached Prefix",
+Lesson: every value checked against double sums at 1e-4 plus 1e-3 relative):
+  fp32 inputs:  |got - ref| <= 1e-4 + 1e-3 |ref|
+  bf16 inputs:  |got - ref| <= 1e-5 + 2^-8 * A, with ref and A from the oracle
+                on the bf16-rounded inputs and A = sum_j w_j |V_j| (the oracle
+                run on |V|).  Scores of bf16 inputs are exact products summed
+                in fp32; the one bf16-specific rounding is that of each
+                probability to bf16 before the PV product (relative <= 2^-9),
+                which moves the output by at most 2^-9 * A.  The bound allows
+                twice that.
+A NaN or inf anywhere fails.  The output is poisoned with quiet NaN before
+each call and surrounded by canary guard bands that must survive.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_prefill_flash_amd as cpf
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+HQ, HKV, D = 32, 8, 64
+TOL_F32 = (1e-4, 1e-3)
+BF16_ABS, BF16_REL_OF_A = 1e-5, 2.0 ** -8
+POISON = 0x7FC00000
+CANARY = 0x7FC0DEAD
+GUARD = 4096  # floats on each side of out
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def to_gpu(x, dtype):
+    """numpy float32 -> device tensor of `dtype` (bf16 rounds to nearest even)."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev())
+    bits = synth.to_bf16_bits(x)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev())
+
+
+def oracle_inputs(x, dtype):
+    return x if dtype == "f32" else synth.bf16_bits_to_f32(synth.to_bf16_bits(x))
+
+
+def run_gpu(q, k, v, P, dtype, stream=None):
+    """Call the library with a poisoned, guarded output; returns numpy out."""
+    C = q.shape[0]
+    qd, kd, vd = to_gpu(q, dtype), to_gpu(k, dtype), to_gpu(v, dtype)
+    n = C * HQ * D
+    buf = torch.empty(n + 2 * GUARD, dtype=torch.int32, device=dev())
+    buf[:GUARD] = CANARY - (1 << 32) if CANARY >= (1 << 31) else CANARY
+    buf[GUARD + n:] = buf[0]
+    buf[GUARD:GUARD + n] = POISON
+    out = buf[GUARD:GUARD + n].view(torch.float32).view(C, HQ, D)
+    cpf.attn_prefill(qd, kd, vd, out=out, P=P, stream=stream)
+    torch.cuda.synchronize()
+    raw = buf.cpu().numpy().view(np.uint32)
+    assert np.all(raw[:GUARD] == CANARY) and np.all(raw[GUARD + n:] == CANARY), "write outside out"
+    return raw[GUARD:GUARD + n].view(np.float32).reshape(C, HQ, D).copy()
+
+
+def check_close(got, ref, dtype, what="", absref=None):
+    """Element-wise tolerance check; absref (bf16 only) is the oracle on |V|."""
+    g = got.astype(np.float64)
+    r = ref.astype(np.float64)
+    err = np.abs(g - r)
+    if dtype == "f32":
+        tol = TOL_F32[0] + TOL_F32[1] * np.abs(r)
+    else:
+        tol = BF16_ABS + BF16_REL_OF_A * absref.astype(np.float64)
+    bad = ~(err <= tol)
+    if bad.any():
+        idx = np.argwhere(bad)
+        i0 = tuple(idx[0])
+        pytest.fail("%s: %d of %d elements out of tolerance; first %s got %r ref %r; max abs err %g"
+                    % (what, bad.sum(), bad.size, i0, got[i0], ref[i0], np.nanmax(err)))
+    return float(err.max()) if err.size else 0.0
+
+
+@functools.lru_cache(maxsize=None)
+def case(name, C, P, dtype):
+    """(q, k, v, plants, ref) for a named workload; ref from the oracle."""
+    plants = []
+    if name == "planted":
+        q, k, v, plants = synth.case_planted_chunk(C, P, 100 if (C, P) == (17, 31) else 1000 + C + P, 3)
+    elif name == "plain":
+        q, k, v = synth.case_plain(C, P, 200 if (C, P) == (2048, 2048) else 3000 + C + 7 * P)
+    elif name == "lastkey":
+        q, k, v, plants = synth.case_last_key(C, P, 400)
+    elif name == "monotone":
+        q, k, v = synth.case_monotone(C, P)
+    else:
+        raise KeyError(name)
+    qo, ko, vo = oracle_inputs(q, dtype), oracle_inputs(k, dtype), oracle_inputs(v, dtype)
+    ref = oracle.attn_prefill(qo, ko, vo, P)
+    absref = oracle.attn_prefill(qo, ko, np.abs(vo), P) if dtype == "bf16" else None
+    return q, k, v, plants, ref, absref
+
+
+def full_check(name, C, P, dtype):
+    q, k, v, plants, ref, absref = case(name, C, P, dtype)
+    got = run_gpu(q, k, v, P, dtype)
+    check_close(got, ref, dtype, "%s C=%d P=%d %s" % (name, C, P, dtype), absref)
+    return q, k, v, plants, got
+
+
+# --- the configurations of the workload -------------------------------------
+
+def test_cfg1_planted_chunk_c17_p31():
+    q, k, v, plants, got = full_check("planted", 17, 31, "f32")
+    for p in plants:   # planted rows of head 0: exactly 4.0
+        assert np.all(got[p - 31, 0] == np.float32(4.0)), (p, got[p - 31, 0, :4])
+
+
+def test_cfg2_serving_chunk_c2048_p2048():
+    full_check("plain", 2048, 2048, "f32")
+
+
+@pytest.mark.parametrize("T", [1, 17, 33, 257, 512, 2048])
+def test_cfg3_prompt_prefill_p0(T):
+    q, k, v, _, got = full_check("plain", T, 0, "f32")
+    # row 0 sees one key: probability exactly 1, output equals V row 0 bitwise
+    for h in range(HQ):
+        assert np.array_equal(got[0, h], v[0, h // 4]), h
+
+
+def test_cfg4_long_prefix_last_key_c512_p15872():
+    q, k, v, plants, got = full_check("lastkey", 512, 15872, "f32")
+    assert np.all(got[511, 0] == np.float32(4.0))
+
+
+def test_cfg5_bf16_c4096_p28672_sampled():
+    """Full size, every head of 40 rows (first, last, both sides of every
+    1024-row boundary, a seeded spread) against the oracle row by row; the
+    whole output must be finite."""
+    C, P = 4096, 28672
+    q, k, v = synth.case_plain(C, P, 500)
+    got = run_gpu(q, k, v, P, "bf16")
+    assert np.all(np.isfinite(got))
+    rows = sorted({0, 1, 7, 8, 31, 32, 1023, 1024, 2047, 2048, 3071, 3072, 4064, 4094, 4095}
+                  | set(int(x) for x in synth.splitmix64(507, 25) % np.uint64(C)))
+    rr = np.repeat(np.array(rows), HQ)
+    hh = np.tile(np.arange(HQ), len(rows))
+    qo, ko, vo = oracle_inputs(q, "bf16"), oracle_inputs(k, "bf16"), oracle_inputs(v, "bf16")
+    ref = oracle.attn_rows(qo, ko, vo, P, rr, hh)
+    absref = oracle.attn_rows(qo, ko, np.abs(vo), P, rr, hh)
+    check_close(got[rr, hh], ref, "bf16", "bf16 C=4096 P=28672 sampled", absref)
+
+
+# --- the page's edge grid and launch-plan coverage ----------------------------
+
+@pytest.mark.parametrize("C", [1, 17, 33])
+@pytest.mark.parametrize("P", [31, 1000])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_edge_grid(C, P, dtype):
+    q, k, v, plants, got = full_check("planted", C, P, dtype)
+    if dtype == "f32":
+        for p in plants:
+            assert np.all(got[p - P, 0] == np.float32(4.0))
+
+
+@pytest.mark.parametrize("C,P", [(255, 3), (256, 700), (600, 0), (1000, 13), (1024, 1), (1500, 100),
+                                 (2049, 7), (2100, 0)])
+def test_every_launch_variant(C, P):
+    """Covers the 1x4, 2x4 and 4x2 workgroup shapes, paired and unpaired
+    row tiles, an odd number of tiles and ragged last tiles."""
+    full_check("plain", C, P, "f32")
+
+
+@pytest.mark.parametrize("C,P", [(300, 1000), (1100, 50)])
+def test_bf16_full_compare(C, P):
+    full_check("plain", C, P, "bf16")
+
+
+def test_every_row_max_in_its_last_tile():
+    """Head-0 scores grow with key position, so every row's maximum is its
+    own diagonal key (met last); a missing rescale fails here."""
+    full_check("monotone", 150, 200, "f32")
+
+
+def test_zero_length_chunk_is_a_noop():
+    q = torch.empty(0, HQ, D, device=dev())
+    k = torch.randn(5, HKV, D, device=dev())
+    out = cpf.attn_prefill(q, k, k.clone())
+    torch.cuda.synchronize()
+    assert out.shape == (0, HQ, D)
+
+
+def test_deterministic_over_ten_launches():
+    """Bitwise equal outputs over repeated launches (a race on the LDS tiles
+    or the split merge would show up as run-to-run differences)."""
+    for (C, P, dt) in [(17, 31, "f32"), (700, 300, "f32"), (2048, 64, "bf16")]:
+        q, k, v = synth.case_plain(C, P, 7700 + C)
+        qd, kd, vd = to_gpu(q, dt), to_gpu(k, dt), to_gpu(v, dt)
+        first = cpf.attn_prefill(qd, kd, vd).cpu()
+        for _ in range(9):
+            again = cpf.attn_prefill(qd, kd, vd).cpu()
+            assert torch.equal(first.view(torch.int32), again.view(torch.int32)), (C, P, dt)
+
+
+def test_side_stream():
+    C, P = 64, 100
+    q, k, v, _, ref, _ = case("plain", C, P, "f32")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = run_gpu(q, k, v, P, "f32", stream=s)
+    check_close(got, ref, "f32", "side stream")
+
+
+def test_binding_errors_on_gpu_tensors():
+    q = torch.zeros(4, HQ, D, device=dev())
+    k = torch.zeros(6, HKV, D, device=dev())
+    flat = torch.zeros(4 * HQ * D + 1, device=dev())
+    mis = flat[1:].view(4, HQ, D)            # 4 bytes off 16-byte alignment
+    with pytest.raises(cpf.AttnError) as e:
+        cpf.attn_prefill(mis, k, k.clone())
+    assert e.value.code == 4
+    with pytest.raises(cpf.AttnError) as e:  # out overlapping q
+        cpf.attn_prefill(q, k, k.clone(), out=q)
+    assert e.value.code == 6
