@@ -161,11 +161,16 @@ def sampled_parity(got, q, k, v, P, dt):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="keep calling for at least this long before timing (lets the GPU clock settle)")
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run a plain elementwise copy of this many MiB three times "
+                         "(reference kernel of known traffic for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -189,8 +194,13 @@ def main():
     out = torch.empty((C, 32, 64), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    for _ in range(max(args.warmup, 1)):
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < max(args.warmup, 1) or time.perf_counter() - t_w < args.warmup_seconds:
         cpf.attn_prefill(qd, kd, vd, out=out, P=P, stream=stream)
+        n_w += 1
+        if n_w % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ok, maxerr = (True, None) if args.no_check else sampled_parity(out.cpu().numpy(), q, k, v, P, dt)
     if not ok:
@@ -225,6 +235,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": n_w,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -238,6 +249,13 @@ def main():
                      "kernel": KERNEL_NAME, "kernel_ms": round(kernel_ms, 5)},
         "parity": {"sampled_rows_ok": ok, "max_abs_err": maxerr},
     }
+    if args.calibrate_copy_mib > 0:
+        src = torch.ones(args.calibrate_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)   # reads and writes calibrate_copy_mib MiB each
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = src.numel() * 4
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(name, q, k, v, P, dt)
     print(json.dumps(result))
