@@ -31,7 +31,7 @@ def flags(extra=()) -> list:
     return [
         "--offload-arch=" + ARCH,
         "-O3",
-        "-std=c++17",
+        "-std=c++20",
         "-fPIC",
         "-shared",
         "-Wall",

@@ -77,32 +77,45 @@ template <> struct Elem<__bf16> {
     static constexpr int kBytes = 2;
 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
 // Tile geometry for a workgroup of NW row-waves x KS key-split waves.
+//
+// LDS holds each staged K and V tile as unpadded key-major rows (256 B fp32,
+// 128 B bf16), in two stages.  Inside a row the 16-byte chunks are permuted
+// by XOR with a per-row code so that the MFMA operand reads (32 lanes on 32
+// different keys, same chunk) and the bf16 transposed V reads (16 lanes on a
+// 4-key x 16-dim block) spread over all LDS banks; unpadded rows let each
+// direct global->LDS load instruction fill 1 KiB of whole rows.
 template <typename T, int NW, int KS>
 struct Geo {
     static constexpr int kNB = KS > 2 ? KS : 2;      // 32-key sub-blocks per staged tile
     static constexpr int kBK = 32 * kNB;             // keys per staged tile
     static constexpr int kThreads = 64 * NW * KS;
+    static constexpr int kWaves = NW * KS;
     static constexpr int kRows = 8 * NW;             // chunk rows per work item
-    static constexpr int kElemsPerChunk = 16 / Elem<T>::kBytes;   // 16-byte global loads
-    static constexpr int kChunksPerRow = kD / kElemsPerChunk;
-    static constexpr int kChunks = kBK * kChunksPerRow / kThreads; // per tensor per thread
-    static_assert(kBK * kChunksPerRow % kThreads == 0, "tile load must divide evenly");
-    // LDS layout, in elements of T.
-    //  fp32: K[BK][68] and V[BK][68], both key-major (row padding of 16 B).
-    //  bf16: K[BK][72] key-major (padding 16 B) and V^T[64][BK+4] dim-major
-    //        (padding 8 B), so a lane's eight PV operands are two 8-byte reads.
-    static constexpr int kKStride = kD + 16 / Elem<T>::kBytes;
-    static constexpr bool kVT = sizeof(T) == 2;
-    static constexpr int kVStride = kVT ? kBK + 4 : kD + 4;
-    static constexpr int kKElems = kBK * kKStride;
-    static constexpr int kVElems = kVT ? kD * kVStride : kBK * kVStride;
-    static constexpr int kStageBytes = (kKElems + kVElems) * Elem<T>::kBytes;
+    static constexpr int kRowBytes = kD * Elem<T>::kBytes;
+    static constexpr int kTileBytes = kBK * kRowBytes;                // one tensor, one stage
+    static constexpr int kStageBytes = 2 * kTileBytes;                // K then V
+    static constexpr int kRowsPerLoad = 1024 / kRowBytes;             // rows per 64-lane 16 B load
+    static constexpr int kLoadsPerTile = 2 * kBK / kRowsPerLoad;      // K and V
+    static constexpr int kLoadsPerWave = (kLoadsPerTile + kWaves - 1) / kWaves;
     // Merge buffer for key splits: per (row-wave, split>0) wave, 34 floats/lane.
     static constexpr int kMergeBytes = KS > 1 ? NW * (KS - 1) * 34 * 64 * 4 : 0;
-    static constexpr int kLdsBytes =
-        2 * kStageBytes > kMergeBytes ? 2 * kStageBytes : kMergeBytes;
+    static constexpr int kLdsBytes = 2 * kStageBytes > kMergeBytes ? 2 * kStageBytes : kMergeBytes;
 };
+
+// Row-dependent chunk permutation (XOR code) of a staged K/V row.
+template <typename T>
+__device__ __forceinline__ int chunk_code(int r) {
+    if constexpr (sizeof(T) == 4) {
+        return r & 7;                                   // 16 chunks per row; low 3 bits permuted
+    } else {
+        return ((r & 3) << 1) | ((r >> 2) & 1);         // 8 chunks per row
+    }
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -119,13 +132,12 @@ __global__ void __launch_bounds__(64 * NW * KS)
 attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
                     float* __restrict__ out, int C, int P, int n_row_tiles, int paired) {
     using G = Geo<T, NW, KS>;
-    constexpr int kBK = G::kBK, kNB = G::kNB, kThreads = G::kThreads, kRows = G::kRows;
-    constexpr int kEPC = G::kElemsPerChunk, kCPR = G::kChunksPerRow, kCH = G::kChunks;
+    constexpr int kBK = G::kBK, kNB = G::kNB, kRows = G::kRows, kRB = G::kRowBytes;
     constexpr bool kF32 = sizeof(T) == 4;
 
-    __shared__ __attribute__((aligned(16))) unsigned char lds_raw[G::kLdsBytes];
-    T* const stage0 = reinterpret_cast<T*>(lds_raw);
-    T* const stage1 = reinterpret_cast<T*>(lds_raw + G::kStageBytes);
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[G::kLdsBytes];
+    unsigned char* const stage0 = lds_raw;
+    unsigned char* const stage1 = lds_raw + G::kStageBytes;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -149,6 +161,35 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         items[1] = items[0];
     }
 
+    // ---- K/V tile staging: bounds-checked buffer loads straight into LDS ----
+    // Load instruction i of a tile covers rows (i % (BK/rpl))*rpl .. +rpl-1 of
+    // K (i < BK/rpl) or V; lane L fetches the chunk that belongs at position
+    // L % cpr of row L / cpr.  Rows past the cache end read as zero (the
+    // descriptor's range is the tile's valid rows).
+    constexpr int kCPR = kRB / 16;                  // 16-byte chunks per row
+    constexpr int kRPL = G::kRowsPerLoad;
+    auto issue_tile = [&](int t, unsigned char* stage) {
+        const int key0 = t * kBK;
+        const int valid = min(kBK, total - key0);
+        const uint32_t range = (uint32_t)valid * kHKV * kRB;   // bytes of this tile's rows, all groups
+        const size_t base = (size_t)key0 * kHKV * kD;
+        __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + base), (short)0, range, 0x00020000);
+        __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + base), (short)0, range, 0x00020000);
+        const int rl = lane / kCPR;                 // row within this load
+        const int pc = lane % kCPR;                 // chunk position within the row
+#pragma unroll
+        for (int u = 0; u < G::kLoadsPerWave; ++u) {
+            const int i = wid + u * G::kWaves;
+            if (G::kLoadsPerTile % G::kWaves != 0 && i >= G::kLoadsPerTile) break;
+            const int tensor = i / (kBK / kRPL);
+            const int row = (i % (kBK / kRPL)) * kRPL + rl;
+            const int lc = pc ^ chunk_code<T>(row);     // logical chunk stored at position pc
+            const uint32_t voff = (uint32_t)(row * kHKV + g) * kRB + lc * 16;
+            unsigned char* dst = stage + tensor * G::kTileBytes + (row - rl) * kRB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(tensor ? rv : rk, (lds_void_t*)dst, 16, voff, 0, 0, 0);
+        }
+    };
+
     for (int it = 0; it < nitems; ++it) {
         const int tile = items[it];
         const int i0 = tile * kRows;
@@ -162,6 +203,8 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         const int row = i0w + (n >> 2);
         const int head = g * kGroup + (n & 3);
         const int lim = P + row;                    // this lane's query sees keys <= lim
+
+        issue_tile(0, stage0);
 
         // ---- Q operand (B of S^T = K Q^T), held for the whole key loop ----
         // fp32: qf[s] = q[row][head][32*hh + s] * log2(e)/8, s = 0..31
@@ -189,67 +232,59 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         float m = -INFINITY;     // running max (log2 units)
         float l = 0.f;           // this lane's share of the running denominator
 
-        // ---- K/V tile staging: global -> registers -> LDS ----
-        f4 kreg[kCH], vreg[kCH];
-        auto load_tile = [&](int t) {
+        // ---- per-lane LDS offsets of the MFMA operands (swizzle folded in) ----
+        // The XOR code of a row depends only on the row index mod 8, and every
+        // stage, tile and sub-block offset is a multiple of 8 rows, so each lane's
+        // operand addresses are a handful of fixed offsets plus immediates.
+        //  fp32 K: chunk 8*hh + c of row n           (c = 0..7)
+        //  fp32 V: dwords n and n+32 of row 4*hh + q   (q = 0..3; row + 8*(t/4))
+        //  bf16 K: chunk 2*st + hh of row n          (st = 0..3)
+        //  bf16 V: transposed 4-key x 16-dim blocks, one offset per 32-dim half
+        int koff[kF32 ? 8 : 4];
+        int voff[kF32 ? 4 : 2];
+        if constexpr (kF32) {
 #pragma unroll
-            for (int u = 0; u < kCH; ++u) {
-                const int c = tid + u * kThreads;
-                const int key = t * kBK + c / kCPR;
-                const int col = (c % kCPR) * kEPC;
-                if (key < total) {
-                    const size_t off = ((size_t)key * kHKV + g) * kD + col;
-                    kreg[u] = *reinterpret_cast<const f4*>(kc + off);
-                    vreg[u] = *reinterpret_cast<const f4*>(vc + off);
-                } else {
-                    kreg[u] = f4{0.f, 0.f, 0.f, 0.f};
-                    vreg[u] = f4{0.f, 0.f, 0.f, 0.f};
-                }
+            for (int c = 0; c < 8; ++c) koff[c] = n * kRB + (((8 * hh + c) ^ chunk_code<T>(n)) * 16);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int r = 4 * hh + q4;
+                voff[q4] = r * kRB + (((n >> 2) ^ chunk_code<T>(r)) * 16) + (n & 3) * 4;
             }
-        };
-        auto store_tile = [&](T* stage) {
-            T* Ks = stage;
-            T* Vs = stage + G::kKElems;
+        } else {
 #pragma unroll
-            for (int u = 0; u < kCH; ++u) {
-                const int c = tid + u * kThreads;
-                const int key = c / kCPR;
-                const int col = (c % kCPR) * kEPC;
-                *reinterpret_cast<f4*>(Ks + key * G::kKStride + col) = kreg[u];
-                if constexpr (!G::kVT) {
-                    *reinterpret_cast<f4*>(Vs + key * G::kVStride + col) = vreg[u];
-                } else {
-                    const u16x8 x = __builtin_bit_cast(u16x8, vreg[u]);
-                    uint16_t* vt = reinterpret_cast<uint16_t*>(Vs);
+            for (int st = 0; st < 4; ++st) koff[st] = n * kRB + (((2 * st + hh) ^ chunk_code<T>(n)) * 16);
+            const int grp = (lane >> 4) & 1;
+            const int j = lane & 15;
+            const int r = 4 * hh + (j >> 2);            // row within an 8-row block
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) vt[(col + e) * G::kVStride + key] = x[e];
-                }
+            for (int nt = 0; nt < 2; ++nt) {
+                const int dim = 32 * nt + 16 * grp + 4 * (j & 3);
+                voff[nt] = r * kRB + (((dim >> 3) ^ chunk_code<T>(r)) * 16) + (dim & 4) * 2;
             }
-        };
+        }
 
         // ---- one 32-key sub-block: scores, mask, online softmax, PV ----
-        auto sub_block = [&](const T* stage, int sb, int jb) {
-            const T* Ks = stage;
-            const T* Vs = stage + G::kKElems;
+        // `stage_off` and `sb` are compile-time constants at every call.
+        auto sub_block = [&](auto stage_off, auto sbc, int jb) {
+            constexpr int kStage = decltype(stage_off)::value;
+            constexpr int sb = decltype(sbc)::value;
+            const unsigned char* Ks = lds_raw + kStage + 32 * sb * kRB;
+            const unsigned char* Vs = lds_raw + kStage + G::kTileBytes + 32 * sb * kRB;
             f16v s = {};
             if constexpr (kF32) {
-                const float* kr = reinterpret_cast<const float*>(Ks) + (32 * sb + n) * G::kKStride + 32 * hh;
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const f4 kx = *reinterpret_cast<const f4*>(kr + 4 * c);
+                    const f4 kx = *reinterpret_cast<const f4*>(Ks + koff[c]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         s = __builtin_amdgcn_mfma_f32_32x32x2f32(kx[e], qf[4 * c + e], s, 0, 0, 0);
                 }
             } else {
-                const uint16_t* kr = reinterpret_cast<const uint16_t*>(Ks) + (32 * sb + n) * G::kKStride + 8 * hh;
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
-                    const bf8 kx = __builtin_bit_cast(bf8, *reinterpret_cast<const u16x8*>(kr + 16 * st));
+                    const bf8 kx = __builtin_bit_cast(bf8, *reinterpret_cast<const u16x8*>(Ks + koff[st]));
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kx, qb[st], s, 0, 0, 0);
                 }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[r] *= kScaleLog2;
             }
             // causal mask, only where the sub-block crosses the wave's first row edge
             if (jb + 31 > w_first) {
@@ -263,6 +298,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
 #pragma unroll
             for (int r = 1; r < 16; ++r) bm = fmaxf(bm, s[r]);
             bm = fmaxf(bm, xchg_half(bm));
+            if constexpr (!kF32) bm *= kScaleLog2;      // bf16 scores are raw dot products
             const bool upd = bm > m + kRescaleSlack;
             if (__ballot(upd)) {
                 const float alpha = upd ? fast_exp2(m - bm) : 1.0f;
@@ -279,36 +315,37 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             float ps = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                p[r] = fast_exp2(s[r] - mu);
+                if constexpr (kF32)
+                    p[r] = fast_exp2(s[r] - mu);
+                else
+                    p[r] = fast_exp2(__builtin_fmaf(s[r], kScaleLog2, -mu));
                 ps += p[r];
             }
             l += ps;
             if constexpr (kF32) {
-                const float* vr = reinterpret_cast<const float*>(Vs) + (32 * sb) * G::kVStride + n;
+                // key 8(t/4) + 4hh + t%4 of the sub-block: V[key][n] and V[key][n+32]
 #pragma unroll
                 for (int t4 = 0; t4 < 16; ++t4) {
-                    const int key = 8 * (t4 >> 2) + 4 * hh + (t4 & 3);
-                    const float v0 = vr[key * G::kVStride];
-                    const float v1 = vr[key * G::kVStride + 32];
-                    o0 = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, p[t4], o0, 0, 0, 0);
-                    o1 = __builtin_amdgcn_mfma_f32_32x32x2f32(v1, p[t4], o1, 0, 0, 0);
+                    const float* vr = reinterpret_cast<const float*>(Vs + 8 * (t4 >> 2) * kRB + voff[t4 & 3]);
+                    o0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[0], p[t4], o0, 0, 0, 0);
+                    o1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32], p[t4], o1, 0, 0, 0);
                 }
             } else {
-                const uint16_t* vt = reinterpret_cast<const uint16_t*>(Vs);
+                // Transposed LDS reads: within each 16-lane group, lane j points at
+                // 4 dims of key K0 + j/4 and receives dim D0 + j of keys K0..K0+3,
+                // which is the A operand V^T[dim][key] of the PV MFMA.
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     bf8 pb;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[8 * u + e];
-                    const int kofs = 32 * sb + 16 * u + 4 * hh;
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
-                        const uint16_t* vrow = vt + (32 * nt + n) * G::kVStride + kofs;
-                        const uint64_t lo = *reinterpret_cast<const uint64_t*>(vrow);
-                        const uint64_t hi = *reinterpret_cast<const uint64_t*>(vrow + 8);
-                        const bf4 a0 = __builtin_bit_cast(bf4, lo);
-                        const bf4 a1 = __builtin_bit_cast(bf4, hi);
-                        const bf8 va = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        const unsigned char* a = Vs + 16 * u * kRB + voff[nt];
+                        const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
+                        const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 8 * kRB));
+                        const bf8 va = __builtin_shufflevector(__builtin_bit_cast(bf4, h0), __builtin_bit_cast(bf4, h1),
+                                                               0, 1, 2, 3, 4, 5, 6, 7);
                         if (nt == 0)
                             o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o0, 0, 0, 0);
                         else
@@ -318,24 +355,40 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             }
         };
 
-        // ---- key loop over staged tiles (double-buffered) ----
-        load_tile(0);
-        store_tile(stage0);
+        // this wave's sub-blocks of tile t, read from the stage at byte offset kStage
+        auto consume = [&](auto stage_off, int t) {
+            if (!wave_active) return;
+            [&]<int... I>(std::integer_sequence<int, I...>) {
+                (([&] {
+                     constexpr int sb = KS * I;
+                     const int sbw = sb + wp;           // wp is runtime; sb + wp < kNB
+                     const int jb = t * kBK + 32 * sbw;
+                     if (jb > w_last) return;
+                     // dispatch on the runtime split index so every offset is an immediate
+                     [&]<int... W>(std::integer_sequence<int, W...>) {
+                         ((wp == W ? (sub_block(stage_off, std::integral_constant<int, sb + W>{}, jb), 0) : 0), ...);
+                     }(std::make_integer_sequence<int, KS>{});
+                 }()),
+                 ...);
+            }(std::make_integer_sequence<int, kNB / KS>{});
+        };
+
+        // ---- key loop over staged tiles (double-buffered, unrolled by two) ----
+        // Tile t+1's loads go to the other stage while tile t is consumed; that
+        // stage was last read before the previous barrier.
+        __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile 0 has landed in LDS
         __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            T* cur = (t & 1) ? stage1 : stage0;
-            T* nxt = (t & 1) ? stage0 : stage1;
-            const bool more = t + 1 < ntiles;
-            if (more) load_tile(t + 1);
-            if (wave_active) {
-#pragma unroll
-                for (int sb = wp; sb < kNB; sb += KS) {
-                    const int jb = t * kBK + 32 * sb;
-                    if (jb <= w_last) sub_block(cur, sb, jb);
-                }
-            }
-            if (more) store_tile(nxt);
+        for (int t = 0; t < ntiles; t += 2) {
+            if (t + 1 < ntiles) issue_tile(t + 1, stage1);
+            consume(std::integral_constant<int, 0>{}, t);
+            __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile t+1 has landed
             __syncthreads();
+            if (t + 1 < ntiles) {
+                if (t + 2 < ntiles) issue_tile(t + 2, stage0);
+                consume(std::integral_constant<int, G::kStageBytes>{}, t + 1);
+                __builtin_amdgcn_s_waitcnt(0x3f70);
+                __syncthreads();
+            }
         }
 
         // ---- merge key splits (log-sum-exp), in LDS ----
