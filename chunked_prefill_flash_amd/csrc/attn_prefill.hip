@@ -141,7 +141,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wid = tid >> 6;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps load descriptors scalar
     const int wr = wid % NW;   // row sub-tile of this wave
     const int wp = wid / NW;   // key split of this wave
     const int n = lane & 31;   // query slot
