@@ -447,7 +447,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
 // ---------------------------------------------------------------------------
 // Host side: argument checks, launch plan, dispatch.
 // ---------------------------------------------------------------------------
-enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2 };
+enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3 };
 
 struct Plan {
     int rows, ks, grid, threads, per_wg, bk, lds, variant, n_row_tiles, paired;
@@ -472,9 +472,13 @@ Plan make_plan(int C, int variant) {
     return p;
 }
 
+// Long chunks: 32 rows x 4 heads per work item; fp32 splits each 128-key tile
+// over 4 waves (16-wave workgroups, 4 waves per SIMD), bf16 over 2 (its LDS
+// and registers allow two 8-wave workgroups per CU).  Medium chunks: 16 rows,
+// 4 key splits.  Short chunks: 8 rows, 4 key splits.
 template <typename T>
 Plan choose_plan(int C) {
-    if (C >= 1024) return make_plan<T, 4, 2>(C, kV_4x2);
+    if (C >= 1024) return sizeof(T) == 4 ? make_plan<T, 4, 4>(C, kV_4x4) : make_plan<T, 4, 2>(C, kV_4x2);
     if (C >= 256) return make_plan<T, 2, 4>(C, kV_2x4);
     return make_plan<T, 1, 4>(C, kV_1x4);
 }
@@ -501,6 +505,7 @@ hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, 
     switch (p.variant) {
         case kV_4x2: return launch<T, 4, 2>(p, q, k, v, out, C, P, stream);
         case kV_2x4: return launch<T, 2, 4>(p, q, k, v, out, C, P, stream);
+        case kV_4x4: return launch<T, 4, 4>(p, q, k, v, out, C, P, stream);
         default: return launch<T, 1, 4>(p, q, k, v, out, C, P, stream);
     }
 }
