@@ -43,6 +43,9 @@ WORKLOADS = {
     "t2048_p0_f32": (2048, 0, "f32", 300, "fp32 plain causal prompt prefill T=2048, P=0"),
     "c4096_p28672_bf16": (4096, 28672, "bf16", 500,
                           "bf16 q/k/v, fp32 accumulation and output, C=4096 at P=28672 (32768 KV positions)"),
+    "c2048_p2048_f32_paged16": (2048, 2048, "f32", 200,
+                                "fp32 C=2048 at P=2048 with the cache in shuffled 16-position pages "
+                                "(block table, 3 spare pages), q/k/v i.i.d. N(0,1)"),
 }
 DEFAULT = "c2048_p2048_f32"
 KERNEL_NAME = "attn_prefill_kernel"
@@ -193,11 +196,24 @@ def main():
     qd, kd, vd = to_device(q, dt, dev), to_device(k, dt, dev), to_device(v, dt, dev)
     out = torch.empty((C, 32, 64), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    paged = "paged" in name
+    if paged:
+        import synth
+        page = int(name.rsplit("paged", 1)[1])
+        kp, vp, table = synth.to_pages(k, v, page, 5600 + page)
+        kpd, vpd = to_device(kp, dt, dev), to_device(vp, dt, dev)
+        tabd = torch.from_numpy(table).to(dev)
+
+    def call():
+        if paged:
+            cpf.attn_prefill_paged(qd, kpd, vpd, tabd, P, out=out, stream=stream)
+        else:
+            cpf.attn_prefill(qd, kd, vd, out=out, P=P, stream=stream)
 
     t_w = time.perf_counter()
     n_w = 0
     while n_w < max(args.warmup, 1) or time.perf_counter() - t_w < args.warmup_seconds:
-        cpf.attn_prefill(qd, kd, vd, out=out, P=P, stream=stream)
+        call()
         n_w += 1
         if n_w % 10 == 0:
             torch.cuda.synchronize()
@@ -215,7 +231,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        cpf.attn_prefill(qd, kd, vd, out=out, P=P, stream=stream)
+        call()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -226,7 +242,7 @@ def main():
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dt]
-    plan = cpf.plan(C, P, torch.float32 if dt == "f32" else torch.bfloat16)
+    plan = cpf.plan(C, P, torch.float32 if dt == "f32" else torch.bfloat16, paged=paged)
 
     result = {
         "metric": METRIC if name == DEFAULT else "causal attn TFLOP/s (%s)" % name,

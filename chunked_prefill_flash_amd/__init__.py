@@ -20,7 +20,7 @@ import os
 
 import torch  # imported first so the library binds to torch's HIP runtime
 
-__all__ = ["attn_prefill", "validate", "plan", "status_string", "library_path", "load_library",
+__all__ = ["attn_prefill", "attn_prefill_paged", "validate", "paged_validate", "plan", "status_string", "library_path", "load_library",
            "flops", "visible_pairs", "AttnError", "EXPORTED_SYMBOLS", "HQ", "HKV", "D"]
 
 HQ, HKV, D = 32, 8, 64
@@ -30,7 +30,7 @@ _lib = None
 
 # Every function include/attn_prefill.h declares.
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_status_string", "attn_prefill_validate", "attn_prefill_plan",
-                    "attn_prefill_version")
+                    "attn_prefill_version", "attn_prefill_paged", "attn_prefill_paged_validate")
 
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_NULL_PTR", 3: "ATTN_ERR_UNSUPPORTED_DTYPE",
@@ -65,7 +65,11 @@ def load_library():
     lib.attn_prefill.restype = i
     lib.attn_prefill_validate.argtypes = [vp, vp, vp, vp, i, i, i]
     lib.attn_prefill_validate.restype = i
-    lib.attn_prefill_plan.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_int)]
+    lib.attn_prefill_plan.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_int)]
+    lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, i, i, vp, i, i, i, vp]
+    lib.attn_prefill_paged.restype = i
+    lib.attn_prefill_paged_validate.argtypes = [vp, vp, vp, vp, i, i, vp, i, i, i]
+    lib.attn_prefill_paged_validate.restype = i
     lib.attn_prefill_plan.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -84,11 +88,18 @@ def validate(q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, C: int, P: int, d
     return int(load_library().attn_prefill_validate(q_ptr, k_ptr, v_ptr, out_ptr, C, P, dtype_code))
 
 
-def plan(C: int, P: int, dtype=torch.float32) -> dict:
+def paged_validate(q_ptr: int, kp_ptr: int, vp_ptr: int, table_ptr: int, num_blocks: int, page_size: int,
+                   out_ptr: int, C: int, P: int, dtype_code: int) -> int:
+    """Raw argument check of attn_prefill_paged (no GPU work); returns the status code."""
+    return int(load_library().attn_prefill_paged_validate(q_ptr, kp_ptr, vp_ptr, table_ptr, num_blocks,
+                                                          page_size, out_ptr, C, P, dtype_code))
+
+
+def plan(C: int, P: int, dtype=torch.float32, paged: bool = False) -> dict:
     """The launch decomposition the library uses for (C, P, dtype)."""
     code = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     arr = (ctypes.c_int * 8)()
-    st = load_library().attn_prefill_plan(C, P, code, arr)
+    st = load_library().attn_prefill_plan(C, P, code, int(bool(paged)), arr)
     if st != 0:
         raise AttnError(st, "attn_prefill_plan")
     keys = ("rows_per_item", "key_splits", "grid", "threads", "items_per_workgroup", "keys_per_tile",
@@ -140,4 +151,42 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
                               s.cuda_stream)
     if st != 0:
         raise AttnError(st, "attn_prefill")
+    return out
+
+
+def attn_prefill_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                       P: int, out: torch.Tensor | None = None,
+                       stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Causal GQA attention of q [C][32][64] against a paged cache.
+
+    k_pages, v_pages: [numBlocks][pageSize][8][64], same dtype as q;
+    block_table: int32 with at least ceil((P+C)/pageSize) physical page indices.
+    Cache position t lives at slot t % pageSize of page block_table[t // pageSize].
+    """
+    if q.dtype not in DTYPES or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("q, k_pages, v_pages must share one dtype in %s" % list(DTYPES))
+    if q.dim() != 3 or q.shape[1:] != (HQ, D):
+        raise ValueError("q must be [C][32][64], got %s" % tuple(q.shape))
+    if k_pages.dim() != 4 or k_pages.shape[2:] != (HKV, D) or v_pages.shape != k_pages.shape:
+        raise ValueError("pages must be [numBlocks][pageSize][8][64], got %s and %s"
+                         % (tuple(k_pages.shape), tuple(v_pages.shape)))
+    C = q.shape[0]
+    num_blocks, page_size = k_pages.shape[0], k_pages.shape[1]
+    if block_table.dtype != torch.int32 or block_table.dim() != 1 or \
+            block_table.shape[0] < -(-(P + C) // page_size):
+        raise ValueError("block_table must be int32 with at least ceil((P+C)/pageSize) entries")
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if out is None:
+        out = torch.empty((C, HQ, D), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.shape != (C, HQ, D) or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous float32 GPU tensor [C][32][64]")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_prefill_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                                    num_blocks, page_size, out.data_ptr(), C, P, DTYPES[q.dtype], s.cuda_stream)
+    if st != 0:
+        raise AttnError(st, "attn_prefill_paged")
     return out

@@ -127,10 +127,19 @@ __device__ __forceinline__ float xchg_half(float x) {
 // ---------------------------------------------------------------------------
 // The kernel.  One workgroup = one KV group g and one or two row tiles.
 // ---------------------------------------------------------------------------
-template <typename T, int NW, int KS>
+// Paged cache description ("FlashAttention and inference kernels", section
+// PagedAttention): position t lives at slot t % page_size of physical page
+// table[t / page_size]; kc/vc then point at [num_blocks][page_size][8][64].
+struct PagedCache {
+    const int* table;
+    int page_size;
+    int num_blocks;
+};
+
+template <typename T, int NW, int KS, bool PAGED>
 __global__ void __launch_bounds__(64 * NW * KS)
 attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
-                    float* __restrict__ out, int C, int P, int n_row_tiles, int paired) {
+                    float* __restrict__ out, int C, int P, int n_row_tiles, int paired, PagedCache pg) {
     using G = Geo<T, NW, KS>;
     constexpr int kBK = G::kBK, kNB = G::kNB, kRows = G::kRows, kRB = G::kRowBytes;
     constexpr bool kF32 = sizeof(T) == 4;
@@ -164,27 +173,55 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     // ---- K/V tile staging: bounds-checked buffer loads straight into LDS ----
     // Load instruction i of a tile covers rows (i % (BK/rpl))*rpl .. +rpl-1 of
     // K (i < BK/rpl) or V; lane L fetches the chunk that belongs at position
-    // L % cpr of row L / cpr.  Rows past the cache end read as zero (the
-    // descriptor's range is the tile's valid rows).
+    // L % cpr of row L / cpr.  Contiguous cache: the descriptor's range is the
+    // tile's valid rows, so rows past the cache end read as zero.  Paged cache:
+    // the descriptor spans the page pool and a row past the cache end, or one
+    // whose page index is out of range, is given an offset past the range and
+    // reads as zero.
     constexpr int kCPR = kRB / 16;                  // 16-byte chunks per row
     constexpr int kRPL = G::kRowsPerLoad;
-    auto issue_tile = [&](int t, unsigned char* stage) {
+    constexpr int kLPW = G::kLoadsPerWave;
+    const int rl = lane / kCPR;                     // row within one load
+    const int pc = lane % kCPR;                     // chunk position within the row
+    auto load_row = [&](int u) { return ((wid + u * G::kWaves) % (kBK / kRPL)) * kRPL + rl; };
+    // physical page of each of this lane's load rows in tile t (paged cache only)
+    auto lookup_pages = [&](int t, int (&phys)[kLPW]) {
+#pragma unroll
+        for (int u = 0; u < kLPW; ++u) {
+            const int key = t * kBK + load_row(u);
+            phys[u] = key < total ? pg.table[key / pg.page_size] : -1;
+        }
+    };
+    auto issue_tile = [&](int t, unsigned char* stage, const int (&phys)[kLPW]) {
         const int key0 = t * kBK;
-        const int valid = min(kBK, total - key0);
-        const uint32_t range = (uint32_t)valid * kHKV * kRB;   // bytes of this tile's rows, all groups
-        const size_t base = (size_t)key0 * kHKV * kD;
+        uint32_t range;
+        size_t base;
+        if constexpr (PAGED) {
+            range = (uint32_t)((size_t)pg.num_blocks * pg.page_size * kHKV * kRB);
+            base = 0;
+        } else {
+            range = (uint32_t)min(kBK, total - key0) * kHKV * kRB;   // bytes of this tile's rows, all groups
+            base = (size_t)key0 * kHKV * kD;
+        }
         __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + base), (short)0, range, 0x00020000);
         __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + base), (short)0, range, 0x00020000);
-        const int rl = lane / kCPR;                 // row within this load
-        const int pc = lane % kCPR;                 // chunk position within the row
 #pragma unroll
-        for (int u = 0; u < G::kLoadsPerWave; ++u) {
+        for (int u = 0; u < kLPW; ++u) {
             const int i = wid + u * G::kWaves;
             if (G::kLoadsPerTile % G::kWaves != 0 && i >= G::kLoadsPerTile) break;
             const int tensor = i / (kBK / kRPL);
-            const int row = (i % (kBK / kRPL)) * kRPL + rl;
+            const int row = load_row(u);
             const int lc = pc ^ chunk_code<T>(row);     // logical chunk stored at position pc
-            const uint32_t voff = (uint32_t)(row * kHKV + g) * kRB + lc * 16;
+            uint32_t voff;
+            if constexpr (PAGED) {
+                const int key = key0 + row;
+                const int ph = phys[u];
+                voff = (ph >= 0 && ph < pg.num_blocks)
+                           ? (uint32_t)(((size_t)ph * pg.page_size + key % pg.page_size) * kHKV + g) * kRB + lc * 16
+                           : range;
+            } else {
+                voff = (uint32_t)(row * kHKV + g) * kRB + lc * 16;
+            }
             unsigned char* dst = stage + tensor * G::kTileBytes + (row - rl) * kRB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(tensor ? rv : rk, (lds_void_t*)dst, 16, voff, 0, 0, 0);
         }
@@ -204,7 +241,12 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         const int head = g * kGroup + (n & 3);
         const int lim = P + row;                    // this lane's query sees keys <= lim
 
-        issue_tile(0, stage0);
+        int physA[kLPW], physB[kLPW];   // page lookups, two tiles ahead (paged cache)
+        if constexpr (PAGED) lookup_pages(0, physA);
+        issue_tile(0, stage0, physA);
+        if constexpr (PAGED) {
+            if (ntiles > 1) lookup_pages(1, physB);
+        }
 
         // ---- Q operand (B of S^T = K Q^T), held for the whole key loop ----
         // fp32: qf[s] = q[row][head][32*hh + s] * log2(e)/8, s = 0..31
@@ -379,12 +421,22 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile 0 has landed in LDS
         __syncthreads();
         for (int t = 0; t < ntiles; t += 2) {
-            if (t + 1 < ntiles) issue_tile(t + 1, stage1);
+            if (t + 1 < ntiles) {
+                issue_tile(t + 1, stage1, physB);
+                if constexpr (PAGED) {
+                    if (t + 2 < ntiles) lookup_pages(t + 2, physA);
+                }
+            }
             consume(std::integral_constant<int, 0>{}, t);
             __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile t+1 has landed
             __syncthreads();
             if (t + 1 < ntiles) {
-                if (t + 2 < ntiles) issue_tile(t + 2, stage0);
+                if (t + 2 < ntiles) {
+                    issue_tile(t + 2, stage0, physA);
+                    if constexpr (PAGED) {
+                        if (t + 3 < ntiles) lookup_pages(t + 3, physB);
+                    }
+                }
                 consume(std::integral_constant<int, G::kStageBytes>{}, t + 1);
                 __builtin_amdgcn_s_waitcnt(0x3f70);
                 __syncthreads();
@@ -477,36 +529,40 @@ Plan make_plan(int C, int variant) {
 // and registers allow two 8-wave workgroups per CU).  Medium chunks: 16 rows,
 // 4 key splits.  Short chunks: 8 rows, 4 key splits.
 template <typename T>
-Plan choose_plan(int C) {
-    if (C >= 1024) return sizeof(T) == 4 ? make_plan<T, 4, 4>(C, kV_4x4) : make_plan<T, 4, 2>(C, kV_4x2);
+Plan choose_plan(int C, bool paged) {
+    // (the paged fp32 16-wave kernel would spill at 128 VGPRs; it uses 8 waves)
+    if (C >= 1024)
+        return sizeof(T) == 4 && !paged ? make_plan<T, 4, 4>(C, kV_4x4) : make_plan<T, 4, 2>(C, kV_4x2);
     if (C >= 256) return make_plan<T, 2, 4>(C, kV_2x4);
     return make_plan<T, 1, 4>(C, kV_1x4);
 }
 
-Plan plan_for(int C, attn_dtype_t dtype) {
-    return dtype == ATTN_DTYPE_BF16 ? choose_plan<__bf16>(C) : choose_plan<float>(C);
+Plan plan_for(int C, attn_dtype_t dtype, bool paged) {
+    return dtype == ATTN_DTYPE_BF16 ? choose_plan<__bf16>(C, paged) : choose_plan<float>(C, paged);
 }
 
-template <typename T, int NW, int KS>
+template <typename T, int NW, int KS, bool PAGED>
 hipError_t launch(const Plan& p, const void* q, const void* k, const void* v, float* out, int C, int P,
-                  hipStream_t stream) {
+                  PagedCache pg, hipStream_t stream) {
     const T* qq = static_cast<const T*>(q);
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
     int n_row_tiles = p.n_row_tiles, paired = p.paired;
-    void* args[] = {&qq, &kk, &vv, &out, &C, &P, &n_row_tiles, &paired};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_prefill_kernel<T, NW, KS>), dim3(p.grid),
+    void* args[] = {&qq, &kk, &vv, &out, &C, &P, &n_row_tiles, &paired, &pg};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_prefill_kernel<T, NW, KS, PAGED>), dim3(p.grid),
                            dim3(p.threads), args, 0, stream);
 }
 
-template <typename T>
+template <typename T, bool PAGED>
 hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, float* out, int C, int P,
-                    hipStream_t stream) {
+                    PagedCache pg, hipStream_t stream) {
     switch (p.variant) {
-        case kV_4x2: return launch<T, 4, 2>(p, q, k, v, out, C, P, stream);
-        case kV_2x4: return launch<T, 2, 4>(p, q, k, v, out, C, P, stream);
-        case kV_4x4: return launch<T, 4, 4>(p, q, k, v, out, C, P, stream);
-        default: return launch<T, 1, 4>(p, q, k, v, out, C, P, stream);
+        case kV_4x2: return launch<T, 4, 2, PAGED>(p, q, k, v, out, C, P, pg, stream);
+        case kV_2x4: return launch<T, 2, 4, PAGED>(p, q, k, v, out, C, P, pg, stream);
+        case kV_4x4:
+            if constexpr (PAGED && sizeof(T) == 4) return hipErrorInvalidValue;   // never planned
+            else return launch<T, 4, 4, PAGED>(p, q, k, v, out, C, P, pg, stream);
+        default: return launch<T, 1, 4, PAGED>(p, q, k, v, out, C, P, pg, stream);
     }
 }
 
@@ -537,11 +593,11 @@ attn_status_t attn_prefill_validate(const void* q, const void* kCache, const voi
     return ATTN_OK;
 }
 
-attn_status_t attn_prefill_plan(int C, int P, attn_dtype_t dtype, int* plan) {
+attn_status_t attn_prefill_plan(int C, int P, attn_dtype_t dtype, int paged, int* plan) {
     if (!plan) return ATTN_ERR_NULL_PTR;
     if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
     if (C < 0 || P < 0 || P > INT_MAX - C) return ATTN_ERR_INVALID_ARG;
-    const Plan p = plan_for(C > 0 ? C : 1, dtype);
+    const Plan p = plan_for(C > 0 ? C : 1, dtype, paged != 0);
     plan[0] = p.rows;
     plan[1] = p.ks;
     plan[2] = C > 0 ? p.grid : 0;
@@ -557,9 +613,46 @@ attn_status_t attn_prefill(const void* q, const void* kCache, const void* vCache
                            attn_dtype_t dtype, hipStream_t stream) {
     const attn_status_t st = attn_prefill_validate(q, kCache, vCache, out, C, P, dtype);
     if (st != ATTN_OK || C == 0) return st;
-    const Plan p = plan_for(C, dtype);
-    const hipError_t e = dtype == ATTN_DTYPE_BF16 ? dispatch<__bf16>(p, q, kCache, vCache, out, C, P, stream)
-                                                  : dispatch<float>(p, q, kCache, vCache, out, C, P, stream);
+    const Plan p = plan_for(C, dtype, false);
+    const PagedCache none{nullptr, 1, 0};
+    const hipError_t e = dtype == ATTN_DTYPE_BF16
+                             ? dispatch<__bf16, false>(p, q, kCache, vCache, out, C, P, none, stream)
+                             : dispatch<float, false>(p, q, kCache, vCache, out, C, P, none, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_prefill_paged_validate(const void* q, const void* kPages, const void* vPages,
+                                          const int* blockTable, int numBlocks, int pageSize, const float* out,
+                                          int C, int P, attn_dtype_t dtype) {
+    if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
+    if (C < 0 || P < 0 || P > INT_MAX - C || pageSize <= 0 || numBlocks <= 0) return ATTN_ERR_INVALID_ARG;
+    const size_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
+    const size_t pool = (size_t)numBlocks * (size_t)pageSize * kHKV * kD * esz;
+    if (pool > 0xFFFFFFFFull) return ATTN_ERR_INVALID_ARG;     // page pool addressed with 32-bit offsets
+    if (C == 0) return ATTN_OK;
+    if (!q || !kPages || !vPages || !blockTable || !out) return ATTN_ERR_NULL_PTR;
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kPages) |
+                          reinterpret_cast<uintptr_t>(vPages) | reinterpret_cast<uintptr_t>(out);
+    if ((mis & 15u) || (reinterpret_cast<uintptr_t>(blockTable) & 3u)) return ATTN_ERR_MISALIGNED;
+    const size_t nq = (size_t)C * kHQ * kD, out_bytes = nq * 4;
+    const size_t ntab = ((size_t)P + C + pageSize - 1) / pageSize;
+    if (overlaps(out, out_bytes, q, nq * esz) || overlaps(out, out_bytes, kPages, pool) ||
+        overlaps(out, out_bytes, vPages, pool) || overlaps(out, out_bytes, blockTable, ntab * 4))
+        return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+attn_status_t attn_prefill_paged(const void* q, const void* kPages, const void* vPages, const int* blockTable,
+                                 int numBlocks, int pageSize, float* out, int C, int P, attn_dtype_t dtype,
+                                 hipStream_t stream) {
+    const attn_status_t st =
+        attn_prefill_paged_validate(q, kPages, vPages, blockTable, numBlocks, pageSize, out, C, P, dtype);
+    if (st != ATTN_OK || C == 0) return st;
+    const Plan p = plan_for(C, dtype, true);
+    const PagedCache pg{blockTable, pageSize, numBlocks};
+    const hipError_t e = dtype == ATTN_DTYPE_BF16
+                             ? dispatch<__bf16, true>(p, q, kPages, vPages, out, C, P, pg, stream)
+                             : dispatch<float, true>(p, q, kPages, vPages, out, C, P, pg, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -576,6 +669,6 @@ const char* attn_status_string(attn_status_t s) {
     return "ATTN_ERR_UNKNOWN";
 }
 
-int attn_prefill_version(void) { return 100; }
+int attn_prefill_version(void) { return 200; }
 
 }  // extern "C"

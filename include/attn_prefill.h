@@ -95,8 +95,39 @@ attn_status_t attn_prefill_validate(const void* q, const void* kCache, const voi
                                     const float* out, int C, int P, attn_dtype_t dtype);
 
 /*
- * attn_prefill_plan -- the launch decomposition attn_prefill would use for
- * (C, P, dtype), written to the caller's int array plan[8]:
+ * attn_prefill_paged -- the same operation with the key/value cache held in
+ * fixed-size pages ("FlashAttention and inference kernels", section
+ * PagedAttention: cache position t lives at slot t % pageSize of physical page
+ * blockTable[t / pageSize]).
+ *
+ *   kPages, vPages  device pointers, [numBlocks][pageSize][8][64] of dtype,
+ *                   16-byte aligned; numBlocks*pageSize*8*64*sizeof(dtype)
+ *                   must not exceed 2^32-1 bytes
+ *   blockTable      device pointer, int32, at least ceil((P+C)/pageSize)
+ *                   entries, 4-byte aligned; entries are physical page indices
+ *   numBlocks       pages in the pool, > 0
+ *   pageSize        positions per page, > 0
+ *   q, out, C, P, dtype, stream as for attn_prefill
+ *
+ * A table entry outside [0, numBlocks) does not fault: the positions it maps
+ * read as zeros (the result is then not the attention of any cache).  Returns
+ * as attn_prefill; ATTN_ERR_INVALID_ARG also for pageSize <= 0, numBlocks <= 0
+ * or a pool too large for 32-bit offsets; ATTN_ERR_ALIAS if out overlaps q, the
+ * pools or the table.
+ */
+attn_status_t attn_prefill_paged(const void* q, const void* kPages, const void* vPages, const int* blockTable,
+                                 int numBlocks, int pageSize, float* out, int C, int P, attn_dtype_t dtype,
+                                 hipStream_t stream);
+
+/* The argument checks of attn_prefill_paged alone; host-only, no HIP call. */
+attn_status_t attn_prefill_paged_validate(const void* q, const void* kPages, const void* vPages,
+                                          const int* blockTable, int numBlocks, int pageSize, const float* out,
+                                          int C, int P, attn_dtype_t dtype);
+
+/*
+ * attn_prefill_plan -- the launch decomposition attn_prefill (paged == 0) or
+ * attn_prefill_paged (paged != 0) would use for (C, P, dtype), written to the
+ * caller's int array plan[8]:
  *   plan[0] rows per work item (query rows of one KV group per item)
  *   plan[1] waves splitting the key range inside a workgroup
  *   plan[2] workgroups in the grid
@@ -108,7 +139,7 @@ attn_status_t attn_prefill_validate(const void* q, const void* kCache, const voi
  * Host-only, no HIP call.  Returns ATTN_OK or ATTN_ERR_INVALID_ARG /
  * ATTN_ERR_UNSUPPORTED_DTYPE / ATTN_ERR_NULL_PTR (plan == NULL).
  */
-attn_status_t attn_prefill_plan(int C, int P, attn_dtype_t dtype, int* plan);
+attn_status_t attn_prefill_plan(int C, int P, attn_dtype_t dtype, int paged, int* plan);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int attn_prefill_version(void);

@@ -49,6 +49,9 @@ def _load():
         lib.oracle_attn_rows.argtypes = [f, f, f, f, ctypes.c_int, ctypes.c_int, ip, ip,
                                          ctypes.c_int, ctypes.c_int]
         lib.oracle_attn_rows.restype = ctypes.c_int
+        lib.oracle_attn_prefill_paged.argtypes = [f, f, f, ip, ctypes.c_int, ctypes.c_int, f, ctypes.c_int,
+                                                  ctypes.c_int, ctypes.c_int]
+        lib.oracle_attn_prefill_paged.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -103,6 +106,27 @@ def attn_rows(q, k, v, P: int, rows, heads, nthreads: int = 0) -> np.ndarray:
                                   rows.shape[0], nthreads)
     if rc != 0:
         raise RuntimeError("oracle_attn_rows failed with code %d" % rc)
+    return out
+
+
+def attn_prefill_paged(q, k_pages, v_pages, block_table, P: int, nthreads: int = 0) -> np.ndarray:
+    """out[C][32][64] for a paged cache: k_pages/v_pages [numBlocks][pageSize][8][64],
+    block_table[ceil((P+C)/pageSize)] of physical page indices."""
+    q, kp, vp = _f32(q), _f32(k_pages), _f32(v_pages)
+    C = q.shape[0]
+    if q.shape != (C, HQ, D) or kp.ndim != 4 or kp.shape[2:] != (HKV, D) or vp.shape != kp.shape:
+        raise ValueError("bad shapes q %s pages %s %s" % (q.shape, kp.shape, vp.shape))
+    nb, ps = kp.shape[0], kp.shape[1]
+    table = np.ascontiguousarray(block_table, dtype=np.int32)
+    if table.shape[0] < -(-(P + C) // ps):
+        raise ValueError("block table too short")
+    out = np.empty((C, HQ, D), dtype=np.float32)
+    if C == 0:
+        return out
+    rc = _load().oracle_attn_prefill_paged(_ptr(q), _ptr(kp), _ptr(vp), _ptr(table, ctypes.c_int), nb, ps,
+                                           _ptr(out), C, P, nthreads)
+    if rc != 0:
+        raise RuntimeError("oracle_attn_prefill_paged failed with code %d" % rc)
     return out
 
 

@@ -27,9 +27,16 @@
  * float once.  Inputs are float32 arrays; bfloat16 inputs are passed widened
  * to float32 (an exact widening).
  *
+ * Paged caches ("FlashAttention and inference kernels", section PagedAttention):
+ * the cache is cut into pages of pageSize positions; position t lives at slot
+ * t % pageSize of physical page blockTable[t / pageSize].  The paged entry
+ * gathers the logical cache position by position and then computes exactly the
+ * definition above.
+ *
  * Parity pins: see the oracle tests (golden worked example, single visible
  * key, planted 4.0 rows, zero keys giving exact prefix means, convex-hull and
- * permutation invariants, numpy float64 formulation on tiny shapes).
+ * permutation invariants, numpy float64 formulation on tiny shapes; paged
+ * gather against the contiguous layout).
  */
 #include <math.h>
 #include <stddef.h>
@@ -137,6 +144,37 @@ int oracle_attn_rows(const float* q, const float* kc, const float* vc, float* ou
         free(s);
     }
     return bad;
+}
+
+/* Paged cache: kPages/vPages are [numBlocks][pageSize][8][64]; blockTable has
+ * ceil((P+C)/pageSize) entries, each in [0, numBlocks).  Returns 0 on success,
+ * 1 on bad sizes or a table entry out of range, 3 if memory runs out. */
+int oracle_attn_prefill_paged(const float* q, const float* kPages, const float* vPages,
+                              const int* blockTable, int numBlocks, int pageSize, float* out,
+                              int C, int P, int nthreads) {
+    if (C < 0 || P < 0 || pageSize <= 0 || numBlocks < 0) return 1;
+    if (C == 0) return 0;
+    const long T = (long)P + C;
+    const long nblk = (T + pageSize - 1) / pageSize;
+    for (long b = 0; b < nblk; ++b)
+        if (blockTable[b] < 0 || blockTable[b] >= numBlocks) return 1;
+    const size_t row = (size_t)OR_HKV * OR_D;
+    float* kc = (float*)malloc(sizeof(float) * (size_t)T * row);
+    float* vc = (float*)malloc(sizeof(float) * (size_t)T * row);
+    int rc = 3;
+    if (kc && vc) {
+        for (long t = 0; t < T; ++t) {
+            const size_t src = ((size_t)blockTable[t / pageSize] * pageSize + (size_t)(t % pageSize)) * row;
+            for (size_t e = 0; e < row; ++e) {
+                kc[(size_t)t * row + e] = kPages[src + e];
+                vc[(size_t)t * row + e] = vPages[src + e];
+            }
+        }
+        rc = oracle_attn_prefill(q, kc, vc, out, C, P, nthreads);
+    }
+    free(kc);
+    free(vc);
+    return rc;
 }
 
 int oracle_max_threads(void) {

@@ -161,3 +161,29 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Widen bfloat16 bit patterns to float32 exactly."""
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_pages(k: np.ndarray, v: np.ndarray, page_size: int, seed: int, spare_pages: int = 3,
+             fill: float = float("nan")):
+    """Scatter a contiguous cache [T][8][64] into pages [numBlocks][page_size][8][64]
+    in a seeded shuffled order ("FlashAttention and inference kernels",
+    PagedAttention: position t lives at slot t % page_size of physical page
+    table[t // page_size]).  spare_pages unused pages are added; every slot not
+    holding a cache position is `fill` (NaN by default), so reading a wrong page
+    or slot shows up.  Returns (k_pages, v_pages, table int32)."""
+    T = k.shape[0]
+    nlog = -(-T // page_size)
+    nb = nlog + spare_pages
+    order = list(range(nb))
+    r = splitmix64(seed, nb)
+    for t in range(nb - 1, 0, -1):            # Fisher-Yates over the physical pages
+        j = int(r[t] % np.uint64(t + 1))
+        order[t], order[j] = order[j], order[t]
+    table = np.array(order[:nlog], dtype=np.int32)
+    kp = np.full((nb, page_size) + k.shape[1:], fill, dtype=np.float32)
+    vp = np.full((nb, page_size) + v.shape[1:], fill, dtype=np.float32)
+    for b in range(nlog):
+        lo, hi = b * page_size, min(T, (b + 1) * page_size)
+        kp[table[b], : hi - lo] = k[lo:hi]
+        vp[table[b], : hi - lo] = v[lo:hi]
+    return kp, vp, table

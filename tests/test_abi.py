@@ -121,6 +121,34 @@ def test_plan_shapes():
     assert cpf.plan(0, 5)["grid"] == 0
 
 
+def pv(q=A, kp=A + 64 * MB, vp=A + 128 * MB, tab=A + 192 * MB, nb=10, ps=16, out=A + 256 * MB, C=17, P=31,
+       dt=F32):
+    return cpf.paged_validate(q, kp, vp, tab, nb, ps, out, C, P, dt)
+
+
+def test_paged_validate_codes():
+    assert pv() == OK
+    assert pv(dt=BF16) == OK
+    assert pv(dt=5) == DTYPE
+    assert pv(ps=0) == INVALID
+    assert pv(nb=0) == INVALID
+    assert pv(C=-1) == INVALID
+    assert pv(nb=1 << 20, ps=16) == INVALID            # pool beyond 32-bit offsets (16M rows x 2 KiB)
+    assert pv(q=0, kp=0, vp=0, tab=0, out=0, C=0) == OK
+    assert pv(tab=0) == NULLP
+    assert pv(tab=A + 192 * MB + 2) == MISAL
+    assert pv(tab=A + 192 * MB + 4) == OK              # the table needs 4-byte alignment only
+    assert pv(kp=A + 64 * MB + 8) == MISAL
+    assert pv(out=A + 192 * MB, tab=A + 192 * MB) == ALIAS
+    assert pv(out=A + 64 * MB, kp=A + 64 * MB) == ALIAS
+
+
+def test_paged_plan_avoids_the_16_wave_fp32_kernel():
+    p = cpf.plan(2048, 2048, paged=True)
+    assert p["threads"] == 512
+    assert cpf.plan(2048, 2048)["threads"] == 1024
+
+
 def test_plan_errors():
     with pytest.raises(cpf.AttnError):
         cpf.plan(-1, 0)

@@ -253,6 +253,29 @@ def test_rows_entry_matches_full():
         assert np.array_equal(sel[t], full[rows[t], heads[t]])
 
 
+@pytest.mark.parametrize("page_size", [1, 16, 17, 64])
+def test_paged_gather_matches_contiguous_cache(page_size):
+    """A paged cache built by scattering the contiguous cache into shuffled
+    pages (the unused slots hold NaN) gives bit-identical outputs: the gather
+    reproduces the logical cache exactly."""
+    C, P = 17, 70
+    q, k, v, _ = synth.case_planted_chunk(C, P, 9910, 3)
+    kp, vp, table = synth.to_pages(k, v, page_size, 9917)
+    got = oracle.attn_prefill_paged(q, kp, vp, table, P)
+    ref = oracle.attn_prefill(q, k, v, P)
+    assert np.array_equal(got, ref)
+    assert sorted(set(table.tolist())) == sorted(table.tolist())   # a permutation prefix
+
+
+def test_paged_rejects_bad_table():
+    q, k, v = synth.case_plain(3, 5, 9920)
+    kp, vp, table = synth.to_pages(k, v, 4, 9921)
+    bad = table.copy()
+    bad[0] = kp.shape[0]
+    with pytest.raises(RuntimeError):
+        oracle.attn_prefill_paged(q, kp, vp, bad, 5)
+
+
 def test_oracle_rejects_bad_shapes():
     q, k, v = synth.case_plain(3, 4, 7000)
     with pytest.raises(ValueError):
@@ -280,6 +303,8 @@ MUTANTS = {
     "first_max_only": ("if (s[j] > M) M = s[j];", "if (s[j] > M && j < 2) M = s[j];"),
     "value_row_shift": ("const float* vrow = vc + ((size_t)j * OR_HKV + g) * OR_D;",
                         "const float* vrow = vc + ((size_t)(j > 0 ? j - 1 : 0) * OR_HKV + g) * OR_D;"),
+    "paged_slot_shift": ("(size_t)(t % pageSize)) * row;", "(size_t)((t + 1) % pageSize)) * row;"),
+    "paged_block_shift": ("blockTable[t / pageSize] * pageSize", "blockTable[(t + 1) / pageSize] * pageSize"),
 }
 
 
@@ -313,13 +338,38 @@ def run_pins_on(so_path):
     pins it fails.  Called in a child process by the mutation test."""
     run = _mutant_runner(so_path)
     caught = []
-    for pin in PINS:
+    pins = list(PINS) + [_paged_pin(so_path)]
+    for pin in pins:
         try:
             with np.errstate(all="ignore"):
                 pin(run)
         except (AssertionError, ValueError, IndexError):
             caught.append(pin.__name__)
     return caught
+
+
+def _paged_pin(so_path):
+    """The paged gather pin, run on the library at so_path."""
+    lib = ctypes.CDLL(so_path)
+    f = ctypes.POINTER(ctypes.c_float)
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.oracle_attn_prefill_paged.argtypes = [f, f, f, ip, ctypes.c_int, ctypes.c_int, f, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int]
+    lib.oracle_attn_prefill_paged.restype = ctypes.c_int
+    contiguous = _mutant_runner(so_path)
+
+    def pin_paged_gather(run):
+        C, P = 9, 30
+        q, k, v = synth.case_plain(C, P, 9930)
+        kp, vp, table = synth.to_pages(k, v, 16, 9931)
+        out = np.empty_like(q)
+        with np.errstate(all="ignore"):
+            rc = lib.oracle_attn_prefill_paged(q.ctypes.data_as(f), kp.ctypes.data_as(f), vp.ctypes.data_as(f),
+                                               table.ctypes.data_as(ip), kp.shape[0], 16, out.ctypes.data_as(f),
+                                               C, P, 2)
+        assert rc == 0
+        assert np.array_equal(out, contiguous(q, k, v, P))
+    return pin_paged_gather
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
