@@ -20,7 +20,7 @@ import os
 
 import torch  # imported first so the library binds to torch's HIP runtime
 
-__all__ = ["attn_prefill", "attn_prefill_paged", "validate", "paged_validate", "plan", "status_string", "library_path", "load_library",
+__all__ = ["attn_prefill", "attn_prefill_paged", "attn_prefill_rowwise", "validate", "paged_validate", "plan", "status_string", "library_path", "load_library",
            "flops", "visible_pairs", "AttnError", "EXPORTED_SYMBOLS", "HQ", "HKV", "D"]
 
 HQ, HKV, D = 32, 8, 64
@@ -30,7 +30,8 @@ _lib = None
 
 # Every function include/attn_prefill.h declares.
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_status_string", "attn_prefill_validate", "attn_prefill_plan",
-                    "attn_prefill_version", "attn_prefill_paged", "attn_prefill_paged_validate")
+                    "attn_prefill_version", "attn_prefill_paged", "attn_prefill_paged_validate",
+                    "attn_prefill_rowwise")
 
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_NULL_PTR", 3: "ATTN_ERR_UNSUPPORTED_DTYPE",
@@ -63,6 +64,8 @@ def load_library():
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, vp]
     lib.attn_prefill.restype = i
+    lib.attn_prefill_rowwise.argtypes = [vp, vp, vp, vp, i, i, i, vp]
+    lib.attn_prefill_rowwise.restype = i
     lib.attn_prefill_validate.argtypes = [vp, vp, vp, vp, i, i, i]
     lib.attn_prefill_validate.restype = i
     lib.attn_prefill_plan.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_int)]
@@ -118,7 +121,8 @@ def flops(C: int, P: int) -> int:
 
 
 def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
-                 P: int | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+                 P: int | None = None, stream: torch.cuda.Stream | None = None, _entry: str = "attn_prefill"
+                 ) -> torch.Tensor:
     """out[C][32][64] = causal GQA attention of q against the cache (k, v).
 
     q [C][32][64], k and v [P+C][8][64], all float32 or all bfloat16, contiguous,
@@ -147,11 +151,18 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
-        st = lib.attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), C, P, DTYPES[q.dtype],
-                              s.cuda_stream)
+        st = getattr(lib, _entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), C, P, DTYPES[q.dtype],
+                                  s.cuda_stream)
     if st != 0:
-        raise AttnError(st, "attn_prefill")
+        raise AttnError(st, _entry)
     return out
+
+
+def attn_prefill_rowwise(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
+                         P: int | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Same result as attn_prefill by the per-row starter algorithm (a timing
+    baseline: every row re-reads its prefix).  Same arguments."""
+    return attn_prefill(q, k, v, out=out, P=P, stream=stream, _entry="attn_prefill_rowwise")
 
 
 def attn_prefill_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,

@@ -497,6 +497,62 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
 }
 
 // ---------------------------------------------------------------------------
+// Per-row baseline: the algorithm of the starter in "Inference Attention 2"
+// (Starter code): no tiling, one (query row, head) per 32 lanes, each lane
+// holding 2 of the 64 dims, the dot product reduced across the 32 lanes, and
+// the online softmax (m, l, accumulator rescaled by exp(m_old - m_new))
+// updated key by key, so every row walks its whole K/V prefix through the
+// memory system on its own.  A 64-lane wave carries two adjacent rows of one
+// head; a 512-thread block covers 64 rows of one head.  It exists to be timed
+// against the tiled kernel (the page's SPEEDUP) and is checked like it.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p) {
+    if constexpr (sizeof(T) == 4) {
+        return *reinterpret_cast<const float*>(p);
+    } else {
+        return (float)*p;
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(512)
+attn_rowwise_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+                    float* __restrict__ out, int C, int P) {
+    const int h = blockIdx.y;
+    const int g = h / kGroup;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;        // which of the wave's two rows
+    const int d = lane & 31;           // this lane's dims: d and d + 32
+    for (int r = 0; r < 4; ++r) {
+        const int row = blockIdx.x * 64 + wave * 8 + 2 * r + half;
+        if (row >= C) break;           // a whole half-wave leaves together
+        const T* qr = q + ((size_t)row * kHQ + h) * kD;
+        const float q0 = load_elem(qr + d) * kScaleLog2;
+        const float q1 = load_elem(qr + d + 32) * kScaleLog2;
+        float m = -INFINITY, l = 0.f, a0 = 0.f, a1 = 0.f;
+        const int last = P + row;
+        for (int j = 0; j <= last; ++j) {
+            const size_t off = ((size_t)j * kHKV + g) * kD;
+            float dot = q0 * load_elem(kc + off + d) + q1 * load_elem(kc + off + d + 32);
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 32);
+            const float mn = fmaxf(m, dot);
+            const float alpha = fast_exp2(m - mn);   // m = -inf on the first key: 0
+            const float p = fast_exp2(dot - mn);
+            l = alpha * l + p;
+            a0 = alpha * a0 + p * load_elem(vc + off + d);
+            a1 = alpha * a1 + p * load_elem(vc + off + d + 32);
+            m = mn;
+        }
+        float* o = out + ((size_t)row * kHQ + h) * kD;
+        o[d] = a0 / l;
+        o[d + 32] = a1 / l;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side: argument checks, launch plan, dispatch.
 // ---------------------------------------------------------------------------
 enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3 };
@@ -618,6 +674,28 @@ attn_status_t attn_prefill(const void* q, const void* kCache, const void* vCache
     const hipError_t e = dtype == ATTN_DTYPE_BF16
                              ? dispatch<__bf16, false>(p, q, kCache, vCache, out, C, P, none, stream)
                              : dispatch<float, false>(p, q, kCache, vCache, out, C, P, none, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_prefill_rowwise(const void* q, const void* kCache, const void* vCache, float* out, int C, int P,
+                                   attn_dtype_t dtype, hipStream_t stream) {
+    const attn_status_t st = attn_prefill_validate(q, kCache, vCache, out, C, P, dtype);
+    if (st != ATTN_OK || C == 0) return st;
+    const dim3 grid((C + 63) / 64, kHQ);
+    hipError_t e;
+    if (dtype == ATTN_DTYPE_BF16) {
+        const __bf16 *qq = static_cast<const __bf16*>(q), *kk = static_cast<const __bf16*>(kCache),
+                     *vv = static_cast<const __bf16*>(vCache);
+        void* args[] = {&qq, &kk, &vv, &out, &C, &P};
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_rowwise_kernel<__bf16>), grid, dim3(512), args, 0,
+                            stream);
+    } else {
+        const float *qq = static_cast<const float*>(q), *kk = static_cast<const float*>(kCache),
+                    *vv = static_cast<const float*>(vCache);
+        void* args[] = {&qq, &kk, &vv, &out, &C, &P};
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_rowwise_kernel<float>), grid, dim3(512), args, 0,
+                            stream);
+    }
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

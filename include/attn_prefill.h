@@ -119,6 +119,17 @@ attn_status_t attn_prefill_paged(const void* q, const void* kPages, const void* 
                                  int numBlocks, int pageSize, float* out, int C, int P, attn_dtype_t dtype,
                                  hipStream_t stream);
 
+/*
+ * attn_prefill_rowwise -- the same result as attn_prefill, computed by the
+ * per-row algorithm of the starter kernel in "Inference Attention 2" (Starter
+ * code): no tiling, one (row, head) per 32 lanes, the online softmax updated
+ * key by key, every row re-reading its whole K/V prefix.  A baseline to time
+ * the tiled kernel against (the page's SPEEDUP), not a fast path.  Same
+ * arguments, layout, ownership and return codes as attn_prefill.
+ */
+attn_status_t attn_prefill_rowwise(const void* q, const void* kCache, const void* vCache, float* out,
+                                   int C, int P, attn_dtype_t dtype, hipStream_t stream);
+
 /* The argument checks of attn_prefill_paged alone; host-only, no HIP call. */
 attn_status_t attn_prefill_paged_validate(const void* q, const void* kPages, const void* vPages,
                                           const int* blockTable, int numBlocks, int pageSize, const float* out,
