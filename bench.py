@@ -43,6 +43,11 @@ WORKLOADS = {
     "t2048_p0_f32": (2048, 0, "f32", 300, "fp32 plain causal prompt prefill T=2048, P=0"),
     "c4096_p28672_bf16": (4096, 28672, "bf16", 500,
                           "bf16 q/k/v, fp32 accumulation and output, C=4096 at P=28672 (32768 KV positions)"),
+    "c1_p16383_f32_splitkv": (1, 16383, "f32", 800,
+                              "fp32 decode: one token at P=16383 (16384 KV positions), key range split across "
+                              "workgroups and merged; q/k/v i.i.d. N(0,1)"),
+    "c1_p32767_bf16_splitkv": (1, 32767, "bf16", 810,
+                               "bf16 decode: one token at P=32767 (32768 KV positions), split across workgroups"),
     "c2048_p2048_f32_paged16": (2048, 2048, "f32", 200,
                                 "fp32 C=2048 at P=2048 with the cache in shuffled 16-position pages "
                                 "(block table, 3 spare pages), q/k/v i.i.d. N(0,1)"),
@@ -148,7 +153,7 @@ def sampled_parity(got, q, k, v, P, dt):
     C = q.shape[0]
     if dt == "bf16":
         q, k, v = (synth.bf16_bits_to_f32(synth.to_bf16_bits(x)) for x in (q, k, v))
-    rows = np.array(sorted({0, 1, C // 3, C // 2, C - 2, C - 1, 7 % C, (5 * C) // 7}))
+    rows = np.array(sorted({r for r in (0, 1, C // 3, C // 2, C - 2, C - 1, 7 % C, (5 * C) // 7) if 0 <= r < C}))
     rr = np.repeat(rows, 32)
     hh = np.tile(np.arange(32), len(rows))
     ref = oracle.attn_rows(q, k, v, P, rr, hh).astype(np.float64)
@@ -206,8 +211,15 @@ def main():
         kpd, vpd = to_device(kp, dt, dev), to_device(vp, dt, dev)
         tabd = torch.from_numpy(table).to(dev)
 
+    splitkv = "splitkv" in name
+    if splitkv:
+        need, _ = cpf.splitkv_workspace(C, P, torch.float32 if dt == "f32" else torch.bfloat16)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
     def call():
-        if paged:
+        if splitkv:
+            cpf.attn_prefill_splitkv(qd, kd, vd, out=out, P=P, workspace=ws, stream=stream)
+        elif paged:
             cpf.attn_prefill_paged(qd, kpd, vpd, tabd, P, out=out, stream=stream)
         else:
             cpf.attn_prefill(qd, kd, vd, out=out, P=P, stream=stream)
@@ -245,6 +257,9 @@ def main():
     achieved = flop / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dt]
     plan = cpf.plan(C, P, torch.float32 if dt == "f32" else torch.bfloat16, paged=paged)
+    if splitkv:
+        plan = {"splits": cpf.splitkv_workspace(C, P, torch.float32 if dt == "f32" else torch.bfloat16)[1],
+                "kernels": "split attention + merge"}
 
     result = {
         "metric": METRIC if name == DEFAULT else "causal attn TFLOP/s (%s)" % name,
@@ -267,7 +282,16 @@ def main():
                      "kernel": KERNEL_NAME, "kernel_ms": round(kernel_ms, 5)},
         "parity": {"sampled_rows_ok": ok, "max_abs_err": maxerr},
     }
-    if not args.no_speedup and not paged:
+    esz = 4 if dt == "f32" else 2
+    alg_bytes = C * 32 * 64 * esz + 2 * (P + C) * 8 * 64 * esz + C * 32 * 64 * 4
+    if splitkv:
+        # decode is bandwidth-bound: roofline against HBM on the compulsory bytes
+        gbs = alg_bytes / (kernel_ms * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                              "kernel": "attn_prefill_kernel (split) + attn_merge_splits_kernel",
+                              "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": alg_bytes}
+    if not args.no_speedup and not paged and not splitkv:
         # the per-row starter algorithm on the same inputs, same run: the page's SPEEDUP
         out2 = torch.empty_like(out)
         for _ in range(2):

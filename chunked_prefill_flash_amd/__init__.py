@@ -20,7 +20,8 @@ import os
 
 import torch  # imported first so the library binds to torch's HIP runtime
 
-__all__ = ["attn_prefill", "attn_prefill_paged", "attn_prefill_rowwise", "validate", "paged_validate", "plan", "status_string", "library_path", "load_library",
+__all__ = ["attn_prefill", "attn_prefill_paged", "attn_prefill_rowwise", "attn_prefill_splitkv",
+           "splitkv_workspace", "validate", "paged_validate", "plan", "status_string", "library_path", "load_library",
            "flops", "visible_pairs", "AttnError", "EXPORTED_SYMBOLS", "HQ", "HKV", "D"]
 
 HQ, HKV, D = 32, 8, 64
@@ -31,11 +32,11 @@ _lib = None
 # Every function include/attn_prefill.h declares.
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_status_string", "attn_prefill_validate", "attn_prefill_plan",
                     "attn_prefill_version", "attn_prefill_paged", "attn_prefill_paged_validate",
-                    "attn_prefill_rowwise")
+                    "attn_prefill_rowwise", "attn_prefill_splitkv", "attn_prefill_splitkv_workspace")
 
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_NULL_PTR", 3: "ATTN_ERR_UNSUPPORTED_DTYPE",
-          4: "ATTN_ERR_MISALIGNED", 5: "ATTN_ERR_LAUNCH", 6: "ATTN_ERR_ALIAS"}
+          4: "ATTN_ERR_MISALIGNED", 5: "ATTN_ERR_LAUNCH", 6: "ATTN_ERR_ALIAS", 7: "ATTN_ERR_WORKSPACE"}
 
 
 class AttnError(RuntimeError):
@@ -64,6 +65,10 @@ def load_library():
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, vp]
     lib.attn_prefill.restype = i
+    lib.attn_prefill_splitkv.argtypes = [vp, vp, vp, vp, i, i, i, vp, ctypes.c_size_t, vp]
+    lib.attn_prefill_splitkv.restype = i
+    lib.attn_prefill_splitkv_workspace.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int)]
+    lib.attn_prefill_splitkv_workspace.restype = i
     lib.attn_prefill_rowwise.argtypes = [vp, vp, vp, vp, i, i, i, vp]
     lib.attn_prefill_rowwise.restype = i
     lib.attn_prefill_validate.argtypes = [vp, vp, vp, vp, i, i, i]
@@ -200,4 +205,52 @@ def attn_prefill_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
                                     num_blocks, page_size, out.data_ptr(), C, P, DTYPES[q.dtype], s.cuda_stream)
     if st != 0:
         raise AttnError(st, "attn_prefill_paged")
+    return out
+
+
+def splitkv_workspace(C: int, P: int, dtype=torch.float32):
+    """(bytes, splits): the workspace attn_prefill_splitkv needs and its key splits."""
+    code = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    nbytes = ctypes.c_size_t()
+    splits = ctypes.c_int()
+    st = load_library().attn_prefill_splitkv_workspace(C, P, code, ctypes.byref(nbytes), ctypes.byref(splits))
+    if st != 0:
+        raise AttnError(st, "attn_prefill_splitkv_workspace")
+    return int(nbytes.value), int(splits.value)
+
+
+def attn_prefill_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
+                         P: int | None = None, workspace: torch.Tensor | None = None,
+                         stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Same result as attn_prefill with the key range split across workgroups
+    and merged (for short chunks / decode against long prefixes).  workspace:
+    a GPU tensor of at least splitkv_workspace(C, P, dtype)[0] bytes (allocated
+    if None)."""
+    if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype in %s" % list(DTYPES))
+    C = q.shape[0]
+    if P is None:
+        P = k.shape[0] - C
+    if q.dim() != 3 or q.shape[1:] != (HQ, D) or k.shape != (P + C, HKV, D) or v.shape != k.shape:
+        raise ValueError("bad shapes q %s k %s v %s for P=%d" % (tuple(q.shape), tuple(k.shape), tuple(v.shape), P))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if out is None:
+        out = torch.empty((C, HQ, D), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.shape != (C, HQ, D) or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous float32 GPU tensor [C][32][64]")
+    need, _ = splitkv_workspace(C, P, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_prefill_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), C, P, DTYPES[q.dtype],
+                                      workspace.data_ptr(), nbytes, s.cuda_stream)
+    if st != 0:
+        raise AttnError(st, "attn_prefill_splitkv")
     return out

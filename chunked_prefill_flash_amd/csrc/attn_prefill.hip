@@ -136,13 +136,28 @@ struct PagedCache {
     int num_blocks;
 };
 
-template <typename T, int NW, int KS, bool PAGED>
+// Key-range split across workgroups (Flash-Decoding, "FlashAttention and
+// inference kernels"): workgroup split s covers keys [s*len, (s+1)*len) of
+// its row tile and writes unnormalised partials (O, m, l) to `part`, which a
+// merge kernel combines.  n == 0: no split, the kernel writes `out` itself.
+struct KeySplit {
+    float* part;    // [n][C][32][64] O, then [n][C][32][2] (m in log2 units, l)
+    int len;        // keys per split, a multiple of the staged tile
+    int n;          // number of splits
+};
+
+enum Mode { kPlain = 0, kPaged = 1, kSplit = 2 };
+
+template <typename T, int NW, int KS, int MODE>
 __global__ void __launch_bounds__(64 * NW * KS)
 attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
-                    float* __restrict__ out, int C, int P, int n_row_tiles, int paired, PagedCache pg) {
+                    float* __restrict__ out, int C, int P, int n_row_tiles, int paired, PagedCache pg,
+                    KeySplit ks) {
     using G = Geo<T, NW, KS>;
     constexpr int kBK = G::kBK, kNB = G::kNB, kRows = G::kRows, kRB = G::kRowBytes;
     constexpr bool kF32 = sizeof(T) == 4;
+    constexpr bool PAGED = MODE == kPaged;
+    constexpr bool SPLIT = MODE == kSplit;
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[G::kLdsBytes];
     unsigned char* const stage0 = lds_raw;
@@ -156,7 +171,9 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     const int n = lane & 31;   // query slot
     const int hh = lane >> 5;  // half-wave
     const int g = blockIdx.x % kHKV;
-    const int slot = blockIdx.x / kHKV;
+    const int split = SPLIT ? (blockIdx.x / kHKV) % ks.n : 0;
+    const int slot = SPLIT ? blockIdx.x / kHKV / ks.n : blockIdx.x / kHKV;
+    int kb = 0;                // first key of this work item's key range
     const int total = P + C;   // cache positions
 
     int items[2];
@@ -188,12 +205,12 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     auto lookup_pages = [&](int t, int (&phys)[kLPW]) {
 #pragma unroll
         for (int u = 0; u < kLPW; ++u) {
-            const int key = t * kBK + load_row(u);
+            const int key = kb + t * kBK + load_row(u);
             phys[u] = key < total ? pg.table[key / pg.page_size] : -1;
         }
     };
     auto issue_tile = [&](int t, unsigned char* stage, const int (&phys)[kLPW]) {
-        const int key0 = t * kBK;
+        const int key0 = kb + t * kBK;
         uint32_t range;
         size_t base;
         if constexpr (PAGED) {
@@ -232,8 +249,10 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         const int i0 = tile * kRows;
         const int i0w = i0 + 8 * wr;
         const int rows_end = min(i0 + kRows, C);
-        const int kv_end = P + rows_end;
-        const int ntiles = (kv_end + kBK - 1) / kBK;
+        if constexpr (SPLIT) kb = split * ks.len;
+        const int kv_end = SPLIT ? min(P + rows_end, kb + ks.len) : P + rows_end;
+        const int ntiles = kv_end > kb ? (kv_end - kb + kBK - 1) / kBK : 0;
+        if (ntiles == 0) continue;                  // this split lies past every row of the item
         const bool wave_active = i0w < C;
         const int w_first = P + i0w;                // visible limit of the wave's first row
         const int w_last = P + min(i0w + 7, C - 1); // visible limit of its last valid row
@@ -404,7 +423,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                 (([&] {
                      constexpr int sb = KS * I;
                      const int sbw = sb + wp;           // wp is runtime; sb + wp < kNB
-                     const int jb = t * kBK + 32 * sbw;
+                     const int jb = kb + t * kBK + 32 * sbw;
                      if (jb > w_last) return;
                      // dispatch on the runtime split index so every offset is an immediate
                      [&]<int... W>(std::integer_sequence<int, W...>) {
@@ -463,8 +482,8 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     const float* src = mb + (size_t)((wr * (KS - 1) + sp - 1) * 34) * 64 + lane;
                     const float m2 = src[32 * 64];
                     const float l2 = src[33 * 64];
-                    const float mx = fmaxf(m, m2);           // m is finite: split 0 sees key 0
-                    const float a = fast_exp2(m - mx);
+                    const float mx = fmaxf(m, m2);
+                    const float a = m == -INFINITY ? 0.f : fast_exp2(m - mx);
                     const float b = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mx);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -478,7 +497,27 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         }
 
         // ---- epilogue: one division per query, fp32 stores ----
-        if (wp == 0 && wave_active) {
+        if constexpr (SPLIT) {
+            // key split: unnormalised partial O, running max m and denominator l
+            if (wp == 0 && wave_active && row < C) {
+                const float lt = l + xchg_half(l);
+                const size_t qi = ((size_t)split * C + row) * kHQ + head;
+                float* dst = ks.part + qi * kD + 4 * hh;
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    *reinterpret_cast<f4*>(dst + 8 * a) = f4{o0[4 * a], o0[4 * a + 1], o0[4 * a + 2], o0[4 * a + 3]};
+                    *reinterpret_cast<f4*>(dst + 32 + 8 * a) = f4{o1[4 * a], o1[4 * a + 1], o1[4 * a + 2], o1[4 * a + 3]};
+                }
+                if (hh == 0) {
+                    float* ml = ks.part + (size_t)ks.n * C * kHQ * kD + qi * 2;
+                    ml[0] = m;
+                    ml[1] = lt;
+                }
+            } else if (wp == 0 && wave_active) {
+                (void)xchg_half(l);                 // keep the half-wave exchange uniform
+            }
+        } else if (wp == 0 && wave_active) {
+            (void)ks;
             const float lt = l + xchg_half(l);
             const float inv = 1.0f / lt;
             if (row < C) {
@@ -553,12 +592,71 @@ attn_rowwise_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
 }
 
 // ---------------------------------------------------------------------------
+// Merge of key-split partials ("FlashAttention and inference kernels",
+// Exercises, exercise 2): m = max_s m_s, w_s = 2^(m_s - m), out = sum_s w_s O_s /
+// sum_s w_s l_s over the splits a row reaches (s*len <= P + row), so no empty
+// segment takes part.  One wave per (row, head), one lane per dim.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum64(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__global__ void __launch_bounds__(256)
+attn_merge_splits_kernel(const float* __restrict__ part, float* __restrict__ out, int C, int P, int len, int n) {
+    const int qi = blockIdx.x * 4 + (threadIdx.x >> 6);    // (row, head) index
+    if (qi >= C * kHQ) return;                           // whole waves leave together
+    const int row = qi / kHQ;
+    const int lane = threadIdx.x & 63;                   // output dim; also a split index below
+    const int ns = min(n, (P + row) / len + 1);
+    const float* ml = part + (size_t)n * C * kHQ * kD;
+    const size_t stride = (size_t)C * kHQ;              // between splits, in (row, head) units
+    // split maxima, 64 splits at a time (one per lane)
+    float mx = -INFINITY;
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+        const int s = s0 + lane;
+        if (s < ns) mx = fmaxf(mx, ml[(s * stride + qi) * 2]);
+    }
+    mx = wave_max64(mx);
+    float L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+        const int s = s0 + lane;
+        float w = 0.f, wl = 0.f;
+        if (s < ns) {
+            w = fast_exp2(ml[(s * stride + qi) * 2] - mx);
+            wl = w * ml[(s * stride + qi) * 2 + 1];
+        }
+        L += wave_sum64(wl);
+        const int cnt = min(64, ns - s0);
+        const float* src = part + ((size_t)s0 * stride + qi) * kD + lane;
+        int t = 0;
+        for (; t + 8 <= cnt; t += 8) {                   // eight independent loads in flight
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = src[(size_t)(t + u) * stride * kD];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) O += __shfl(w, t + u, 64) * x[u];
+        }
+        for (; t < cnt; ++t) O += __shfl(w, t, 64) * src[(size_t)t * stride * kD];
+    }
+    out[(size_t)qi * kD + lane] = O / L;
+}
+
+// ---------------------------------------------------------------------------
 // Host side: argument checks, launch plan, dispatch.
 // ---------------------------------------------------------------------------
 enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3 };
 
 struct Plan {
     int rows, ks, grid, threads, per_wg, bk, lds, variant, n_row_tiles, paired;
+    int splits, split_len;   // key-range splits across workgroups (0: none)
 };
 
 template <typename T, int NW, int KS>
@@ -597,29 +695,59 @@ Plan plan_for(int C, attn_dtype_t dtype, bool paged) {
     return dtype == ATTN_DTYPE_BF16 ? choose_plan<__bf16>(C, paged) : choose_plan<float>(C, paged);
 }
 
-template <typename T, int NW, int KS, bool PAGED>
+template <typename T, int NW, int KS, int MODE>
 hipError_t launch(const Plan& p, const void* q, const void* k, const void* v, float* out, int C, int P,
-                  PagedCache pg, hipStream_t stream) {
+                  PagedCache pg, KeySplit ksp, hipStream_t stream) {
     const T* qq = static_cast<const T*>(q);
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
     int n_row_tiles = p.n_row_tiles, paired = p.paired;
-    void* args[] = {&qq, &kk, &vv, &out, &C, &P, &n_row_tiles, &paired, &pg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_prefill_kernel<T, NW, KS, PAGED>), dim3(p.grid),
+    void* args[] = {&qq, &kk, &vv, &out, &C, &P, &n_row_tiles, &paired, &pg, &ksp};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_prefill_kernel<T, NW, KS, MODE>), dim3(p.grid),
                            dim3(p.threads), args, 0, stream);
 }
 
-template <typename T, bool PAGED>
+template <typename T, int MODE>
 hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, float* out, int C, int P,
-                    PagedCache pg, hipStream_t stream) {
+                    PagedCache pg, KeySplit ksp, hipStream_t stream) {
     switch (p.variant) {
-        case kV_4x2: return launch<T, 4, 2, PAGED>(p, q, k, v, out, C, P, pg, stream);
-        case kV_2x4: return launch<T, 2, 4, PAGED>(p, q, k, v, out, C, P, pg, stream);
+        case kV_4x2:
+            if constexpr (MODE == kSplit) return hipErrorInvalidValue;   // never planned
+            else return launch<T, 4, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
+        case kV_2x4: return launch<T, 2, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
         case kV_4x4:
-            if constexpr (PAGED && sizeof(T) == 4) return hipErrorInvalidValue;   // never planned
-            else return launch<T, 4, 4, PAGED>(p, q, k, v, out, C, P, pg, stream);
-        default: return launch<T, 1, 4, PAGED>(p, q, k, v, out, C, P, pg, stream);
+            if constexpr (MODE == kSplit || (MODE == kPaged && sizeof(T) == 4)) return hipErrorInvalidValue;
+            else return launch<T, 4, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
+        default: return launch<T, 1, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
     }
+}
+
+// Key splits for the workspace variant: about one workgroup per CU (row tiles
+// x KV groups x splits >= 256; measured faster than 512 or 1024 because each
+// split then streams more tiles), each split at least two staged tiles long;
+// split length a multiple of the staged tile.
+Plan split_plan(int C, int P, attn_dtype_t dtype) {
+    // short chunks: 8-row work items; longer ones: 16 rows (both 4 key-split waves)
+    Plan p = C < 256 ? (dtype == ATTN_DTYPE_BF16 ? make_plan<__bf16, 1, 4>(C, kV_1x4) : make_plan<float, 1, 4>(C, kV_1x4))
+                     : (dtype == ATTN_DTYPE_BF16 ? make_plan<__bf16, 2, 4>(C, kV_2x4) : make_plan<float, 2, 4>(C, kV_2x4));
+    p.paired = 0;
+    p.per_wg = 1;
+    const int total = P + C;
+    const int base = p.n_row_tiles * kHKV;
+    constexpr int kTargetWorkgroups = 256;
+    int s = (kTargetWorkgroups + base - 1) / base;
+    const int most = (total + 2 * p.bk - 1) / (2 * p.bk);
+    s = max(1, min(s, most));
+    int len = (total + s - 1) / s;
+    len = (len + p.bk - 1) / p.bk * p.bk;
+    p.splits = (total + len - 1) / len;
+    p.split_len = len;
+    p.grid = base * p.splits;
+    return p;
+}
+
+size_t split_workspace_bytes(const Plan& p, int C) {
+    return (size_t)p.splits * C * kHQ * (kD + 2) * sizeof(float);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -671,9 +799,54 @@ attn_status_t attn_prefill(const void* q, const void* kCache, const void* vCache
     if (st != ATTN_OK || C == 0) return st;
     const Plan p = plan_for(C, dtype, false);
     const PagedCache none{nullptr, 1, 0};
+    const KeySplit nosplit{nullptr, 0, 0};
     const hipError_t e = dtype == ATTN_DTYPE_BF16
-                             ? dispatch<__bf16, false>(p, q, kCache, vCache, out, C, P, none, stream)
-                             : dispatch<float, false>(p, q, kCache, vCache, out, C, P, none, stream);
+                             ? dispatch<__bf16, kPlain>(p, q, kCache, vCache, out, C, P, none, nosplit, stream)
+                             : dispatch<float, kPlain>(p, q, kCache, vCache, out, C, P, none, nosplit, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_prefill_splitkv_workspace(int C, int P, attn_dtype_t dtype, size_t* bytes, int* splits) {
+    if (!bytes) return ATTN_ERR_NULL_PTR;
+    if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
+    if (C < 0 || P < 0 || P > INT_MAX - C) return ATTN_ERR_INVALID_ARG;
+    if (C == 0) {
+        *bytes = 0;
+        if (splits) *splits = 0;
+        return ATTN_OK;
+    }
+    const Plan p = split_plan(C, P, dtype);
+    *bytes = split_workspace_bytes(p, C);
+    if (splits) *splits = p.splits;
+    return ATTN_OK;
+}
+
+attn_status_t attn_prefill_splitkv(const void* q, const void* kCache, const void* vCache, float* out, int C, int P,
+                                   attn_dtype_t dtype, void* workspace, size_t workspaceBytes,
+                                   hipStream_t stream) {
+    const attn_status_t st = attn_prefill_validate(q, kCache, vCache, out, C, P, dtype);
+    if (st != ATTN_OK || C == 0) return st;
+    const Plan p = split_plan(C, P, dtype);
+    const size_t need = split_workspace_bytes(p, C);
+    if (!workspace) return ATTN_ERR_NULL_PTR;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return ATTN_ERR_MISALIGNED;
+    if (workspaceBytes < need) return ATTN_ERR_WORKSPACE;
+    const size_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
+    const size_t nq = (size_t)C * kHQ * kD, nkv = ((size_t)P + C) * kHKV * kD;
+    if (overlaps(workspace, need, q, nq * esz) || overlaps(workspace, need, kCache, nkv * esz) ||
+        overlaps(workspace, need, vCache, nkv * esz) || overlaps(workspace, need, out, nq * 4))
+        return ATTN_ERR_ALIAS;
+    const PagedCache none{nullptr, 1, 0};
+    const KeySplit ksp{static_cast<float*>(workspace), p.split_len, p.splits};
+    hipError_t e = dtype == ATTN_DTYPE_BF16
+                       ? dispatch<__bf16, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream)
+                       : dispatch<float, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream);
+    if (e != hipSuccess) return ATTN_ERR_LAUNCH;
+    const float* part = static_cast<const float*>(workspace);
+    int len = p.split_len, n = p.splits;
+    void* args[] = {&part, &out, &C, &P, &len, &n};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_merge_splits_kernel), dim3((C * kHQ + 3) / 4),
+                        dim3(256), args, 0, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -728,9 +901,10 @@ attn_status_t attn_prefill_paged(const void* q, const void* kPages, const void* 
     if (st != ATTN_OK || C == 0) return st;
     const Plan p = plan_for(C, dtype, true);
     const PagedCache pg{blockTable, pageSize, numBlocks};
+    const KeySplit nosplit{nullptr, 0, 0};
     const hipError_t e = dtype == ATTN_DTYPE_BF16
-                             ? dispatch<__bf16, true>(p, q, kPages, vPages, out, C, P, pg, stream)
-                             : dispatch<float, true>(p, q, kPages, vPages, out, C, P, pg, stream);
+                             ? dispatch<__bf16, kPaged>(p, q, kPages, vPages, out, C, P, pg, nosplit, stream)
+                             : dispatch<float, kPaged>(p, q, kPages, vPages, out, C, P, pg, nosplit, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -743,6 +917,7 @@ const char* attn_status_string(attn_status_t s) {
         case ATTN_ERR_MISALIGNED: return "ATTN_ERR_MISALIGNED";
         case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH";
         case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS";
+        case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
     }
     return "ATTN_ERR_UNKNOWN";
 }

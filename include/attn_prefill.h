@@ -37,6 +37,8 @@
 #ifndef ATTN_PREFILL_H
 #define ATTN_PREFILL_H
 
+#include <stddef.h>
+
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -61,7 +63,8 @@ typedef enum {
     ATTN_ERR_UNSUPPORTED_DTYPE = 3,/* dtype is not an attn_dtype_t value */
     ATTN_ERR_MISALIGNED = 4,       /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_LAUNCH = 5,           /* the HIP runtime rejected the launch */
-    ATTN_ERR_ALIAS = 6             /* out overlaps q, kCache or vCache */
+    ATTN_ERR_ALIAS = 6,            /* out (or a workspace) overlaps another argument */
+    ATTN_ERR_WORKSPACE = 7         /* workspace smaller than attn_prefill_splitkv_workspace() */
 } attn_status_t;
 
 /*
@@ -129,6 +132,37 @@ attn_status_t attn_prefill_paged(const void* q, const void* kPages, const void* 
  */
 attn_status_t attn_prefill_rowwise(const void* q, const void* kCache, const void* vCache, float* out,
                                    int C, int P, attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * attn_prefill_splitkv -- the same result as attn_prefill, with the key range
+ * of each row tile split across workgroups ("FlashAttention and inference
+ * kernels", Flash-Decoding / split-K): every split writes an unnormalised
+ * partial (O_s, m_s, l_s) per (row, head) to `workspace`, and a second kernel
+ * merges them with weights e^(m_s - m) over the splits each row reaches.  For
+ * short chunks (decode, C = 1..64) against long prefixes, where row tiles x KV
+ * groups alone cannot fill the GPU.
+ *
+ *   workspace       device memory of at least attn_prefill_splitkv_workspace()
+ *                   bytes, 16-byte aligned, not overlapping any argument;
+ *                   owned by the caller; its contents on entry do not matter
+ *                   and are garbage on return.  Calls that share a workspace
+ *                   must be ordered on one stream.
+ *   workspaceBytes  its size in bytes
+ *   other arguments as for attn_prefill
+ *
+ * Returns as attn_prefill; ATTN_ERR_WORKSPACE if workspaceBytes is too small,
+ * ATTN_ERR_NULL_PTR / ATTN_ERR_MISALIGNED / ATTN_ERR_ALIAS for the workspace.
+ */
+attn_status_t attn_prefill_splitkv(const void* q, const void* kCache, const void* vCache, float* out,
+                                   int C, int P, attn_dtype_t dtype, void* workspace, size_t workspaceBytes,
+                                   hipStream_t stream);
+
+/*
+ * attn_prefill_splitkv_workspace -- bytes of workspace attn_prefill_splitkv
+ * needs for (C, P, dtype), and (if splits != NULL) how many key splits it
+ * uses.  Host-only, no HIP call.  C == 0 needs 0 bytes.
+ */
+attn_status_t attn_prefill_splitkv_workspace(int C, int P, attn_dtype_t dtype, size_t* bytes, int* splits);
 
 /* The argument checks of attn_prefill_paged alone; host-only, no HIP call. */
 attn_status_t attn_prefill_paged_validate(const void* q, const void* kPages, const void* vPages,

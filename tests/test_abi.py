@@ -13,7 +13,7 @@ import chunked_prefill_flash_amd as cpf
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, INVALID, NULLP, DTYPE, MISAL, LAUNCH, ALIAS = range(7)
+OK, INVALID, NULLP, DTYPE, MISAL, LAUNCH, ALIAS, WORKSPACE = range(8)
 F32, BF16 = 0, 1
 A = 0x10000000          # fake, 16-byte aligned addresses: never dereferenced
 MB = 1 << 20
@@ -147,6 +147,31 @@ def test_paged_plan_avoids_the_16_wave_fp32_kernel():
     p = cpf.plan(2048, 2048, paged=True)
     assert p["threads"] == 512
     assert cpf.plan(2048, 2048)["threads"] == 1024
+
+
+def test_splitkv_workspace_sizes():
+    nb, ns = cpf.splitkv_workspace(1, 32767)
+    assert ns > 1 and nb == ns * 1 * 32 * 66 * 4
+    nb, ns = cpf.splitkv_workspace(17, 31)
+    assert ns >= 1 and nb == ns * 17 * 32 * 66 * 4
+    assert cpf.splitkv_workspace(0, 10) == (0, 0)
+    # splits never exceed the cache length in staged tiles, and always cover it
+    for C, P in [(1, 0), (1, 100), (5, 4000), (64, 100000), (300, 3000)]:
+        nb, ns = cpf.splitkv_workspace(C, P)
+        assert 1 <= ns <= max(1, (P + C + 63) // 64)
+    with pytest.raises(cpf.AttnError):
+        cpf.splitkv_workspace(-1, 0)
+
+
+def test_splitkv_rejects_small_or_missing_workspace():
+    import ctypes
+    lib = cpf.load_library()
+    need, _ = cpf.splitkv_workspace(4, 1000)
+    args = (A, A + 64 * MB, A + 128 * MB, A + 192 * MB, 4, 1000, F32)
+    assert lib.attn_prefill_splitkv(*args, A + 256 * MB, need - 16, None) == WORKSPACE
+    assert lib.attn_prefill_splitkv(*args, None, need, None) == NULLP
+    assert lib.attn_prefill_splitkv(*args, A + 256 * MB + 4, need, None) == MISAL
+    assert lib.attn_prefill_splitkv(*args, A + 192 * MB, need, None) == ALIAS    # workspace on out
 
 
 def test_plan_errors():
