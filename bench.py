@@ -309,6 +309,27 @@ def main():
                                         "speedup": round(base_ms / kernel_ms, 2),
                                         "baseline": "per-row online softmax, one (row, head) per 32 lanes, "
                                                     "every row re-reads its prefix (the pages' starter)"}
+    if not args.no_speedup and P == 0 and dt == "f32" and not paged and not splitkv:
+        # the three-kernel pipeline with the full score matrix on the same prompt
+        need = cpf.naive_workspace(C)
+        ws_n = torch.empty(need, dtype=torch.uint8, device=dev)
+        out3 = torch.empty_like(out)
+        for _ in range(3):
+            cpf.attn_naive(qd, kd, vd, out=out3, workspace=ws_n, stream=stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        n_base = 10
+        for _ in range(n_base):
+            cpf.attn_naive(qd, kd, vd, out=out3, workspace=ws_n, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        naive_ms = e0.elapsed_time(e1) / n_base
+        result["vs_naive_pipeline"] = {"naive_ms": round(naive_ms, 4), "fused_ms": round(kernel_ms, 5),
+                                       "speedup": round(naive_ms / kernel_ms, 2), "workspace_bytes": need,
+                                       "baseline": "scores -> in-place row softmax -> PV, 32 x T x T fp32 "
+                                                   "score matrix in HBM between the kernels"}
+        del ws_n
     if args.calibrate_copy_mib > 0:
         src = torch.ones(args.calibrate_copy_mib << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -21,7 +21,7 @@ import os
 import torch  # imported first so the library binds to torch's HIP runtime
 
 __all__ = ["attn_prefill", "attn_prefill_paged", "attn_prefill_rowwise", "attn_prefill_splitkv",
-           "splitkv_workspace", "validate", "paged_validate", "plan", "status_string", "library_path", "load_library",
+           "splitkv_workspace", "attn_naive", "naive_workspace", "validate", "paged_validate", "plan", "status_string", "library_path", "load_library",
            "flops", "visible_pairs", "AttnError", "EXPORTED_SYMBOLS", "HQ", "HKV", "D"]
 
 HQ, HKV, D = 32, 8, 64
@@ -32,7 +32,8 @@ _lib = None
 # Every function include/attn_prefill.h declares.
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_status_string", "attn_prefill_validate", "attn_prefill_plan",
                     "attn_prefill_version", "attn_prefill_paged", "attn_prefill_paged_validate",
-                    "attn_prefill_rowwise", "attn_prefill_splitkv", "attn_prefill_splitkv_workspace")
+                    "attn_prefill_rowwise", "attn_prefill_splitkv", "attn_prefill_splitkv_workspace",
+                    "attn_naive", "attn_naive_workspace")
 
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_NULL_PTR", 3: "ATTN_ERR_UNSUPPORTED_DTYPE",
@@ -69,6 +70,10 @@ def load_library():
     lib.attn_prefill_splitkv.restype = i
     lib.attn_prefill_splitkv_workspace.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int)]
     lib.attn_prefill_splitkv_workspace.restype = i
+    lib.attn_naive.argtypes = [vp, vp, vp, vp, i, vp, ctypes.c_size_t, vp]
+    lib.attn_naive.restype = i
+    lib.attn_naive_workspace.argtypes = [i, ctypes.POINTER(ctypes.c_size_t)]
+    lib.attn_naive_workspace.restype = i
     lib.attn_prefill_rowwise.argtypes = [vp, vp, vp, vp, i, i, i, vp]
     lib.attn_prefill_rowwise.restype = i
     lib.attn_prefill_validate.argtypes = [vp, vp, vp, vp, i, i, i]
@@ -253,4 +258,40 @@ def attn_prefill_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out:
                                       workspace.data_ptr(), nbytes, s.cuda_stream)
     if st != 0:
         raise AttnError(st, "attn_prefill_splitkv")
+    return out
+
+
+def naive_workspace(T: int) -> int:
+    """Bytes of score-matrix workspace attn_naive needs (32*T*T*4)."""
+    nbytes = ctypes.c_size_t()
+    st = load_library().attn_naive_workspace(T, ctypes.byref(nbytes))
+    if st != 0:
+        raise AttnError(st, "attn_naive_workspace")
+    return int(nbytes.value)
+
+
+def attn_naive(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Causal prompt prefill (P = 0) by the three-kernel pipeline with the full
+    32 x T x T score matrix in `workspace` (allocated if None).  fp32 only."""
+    if q.dtype != torch.float32 or k.dtype != torch.float32 or v.dtype != torch.float32:
+        raise TypeError("attn_naive takes float32 tensors")
+    T = q.shape[0]
+    if q.shape != (T, HQ, D) or k.shape != (T, HKV, D) or v.shape != k.shape:
+        raise ValueError("q [T][32][64], k and v [T][8][64] expected")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if out is None:
+        out = torch.empty((T, HQ, D), dtype=torch.float32, device=q.device)
+    need = naive_workspace(T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = load_library().attn_naive(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), T,
+                                       workspace.data_ptr(), nbytes, s.cuda_stream)
+    if st != 0:
+        raise AttnError(st, "attn_naive")
     return out

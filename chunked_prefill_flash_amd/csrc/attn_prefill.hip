@@ -650,6 +650,126 @@ attn_merge_splits_kernel(const float* __restrict__ part, float* __restrict__ out
 }
 
 // ---------------------------------------------------------------------------
+// Naive three-kernel pipeline ("Inference Attention 1: The Full Score Matrix",
+// Lesson): prompt prefill (P = 0) as an eager framework runs it, with the whole
+// 32 x T x T fp32 score matrix in a caller workspace between the kernels.
+//  1. scores: S[h][i][j] = q[i][h] . k[j][h/4] / 8, -inf above the diagonal
+//  2. row softmax in place (max subtracted; 0 above the diagonal)
+//  3. weighted sum: out[i][h] = sum_j S[h][i][j] v[j][h/4]
+// It exists to be measured against the fused path: it moves the T x T matrix
+// through memory four times.
+// ---------------------------------------------------------------------------
+constexpr int kNT = 64;   // tile edge of the two matrix products
+
+__global__ void __launch_bounds__(256)
+naive_scores_kernel(const float* __restrict__ q, const float* __restrict__ k, float* __restrict__ S, int T) {
+    const int h = blockIdx.z, g = h / kGroup;
+    const int i0 = blockIdx.y * kNT, j0 = blockIdx.x * kNT;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;   // 4 x 4 outputs per thread
+    float* Sh = S + (size_t)h * T * T;
+    if (j0 > i0 + kNT - 1) {                                   // wholly above the diagonal
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int i = i0 + 4 * ty + a, j = j0 + 4 * tx + b;
+                if (i < T && j < T) Sh[(size_t)i * T + j] = -INFINITY;
+            }
+        return;
+    }
+    __shared__ float qs[kNT][kNT + 1];
+    __shared__ float ks[kNT][kNT + 1];
+    for (int e = threadIdx.x; e < kNT * kNT; e += 256) {
+        const int r = e / kNT, c = e % kNT;
+        qs[r][c] = i0 + r < T ? q[((size_t)(i0 + r) * kHQ + h) * kD + c] : 0.f;
+        ks[r][c] = j0 + r < T ? k[((size_t)(j0 + r) * kHKV + g) * kD + c] : 0.f;
+    }
+    __syncthreads();
+    float acc[4][4] = {};
+    for (int c = 0; c < kD; ++c) {
+        float qa[4], kb4[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) qa[a] = qs[4 * ty + a][c];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) kb4[b] = ks[4 * tx + b][c];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] += qa[a] * kb4[b];
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int i = i0 + 4 * ty + a, j = j0 + 4 * tx + b;
+            if (i < T && j < T) Sh[(size_t)i * T + j] = j <= i ? acc[a][b] * 0.125f : -INFINITY;
+        }
+}
+
+__global__ void __launch_bounds__(256)
+naive_softmax_kernel(float* __restrict__ S, int T) {
+    float* row = S + ((size_t)blockIdx.y * T + blockIdx.x) * T;
+    __shared__ float red[4];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    float mx = -INFINITY;
+    for (int j = threadIdx.x; j < T; j += 256) mx = fmaxf(mx, row[j]);
+    mx = wave_max64(mx);
+    if (lane == 0) red[w] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float sum = 0.f;
+    for (int j = threadIdx.x; j < T; j += 256) {
+        const float e = __expf(row[j] - mx);
+        row[j] = e;
+        sum += e;
+    }
+    sum = wave_sum64(sum);
+    if (lane == 0) red[w] = sum;
+    __syncthreads();
+    const float inv = 1.0f / (red[0] + red[1] + red[2] + red[3]);
+    for (int j = threadIdx.x; j < T; j += 256) row[j] *= inv;
+}
+
+__global__ void __launch_bounds__(256)
+naive_pv_kernel(const float* __restrict__ S, const float* __restrict__ v, float* __restrict__ out, int T) {
+    const int h = blockIdx.y, g = h / kGroup;
+    const int i0 = blockIdx.x * kNT;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;   // rows 4*ty+a, dims 4*tx+b
+    const float* Sh = S + (size_t)h * T * T;
+    __shared__ float ps[kNT][kNT + 1];
+    __shared__ float vs[kNT][kNT + 1];
+    float acc[4][4] = {};
+    for (int j0 = 0; j0 < T; j0 += kNT) {
+        for (int e = threadIdx.x; e < kNT * kNT; e += 256) {
+            const int r = e / kNT, c = e % kNT;
+            ps[r][c] = (i0 + r < T && j0 + c < T) ? Sh[(size_t)(i0 + r) * T + j0 + c] : 0.f;
+            vs[r][c] = j0 + r < T ? v[((size_t)(j0 + r) * kHKV + g) * kD + c] : 0.f;
+        }
+        __syncthreads();
+        for (int c = 0; c < kNT; ++c) {
+            float pa[4], vb[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) pa[a] = ps[4 * ty + a][c];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) vb[b] = vs[c][4 * tx + b];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[a][b] += pa[a] * vb[b];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int i = i0 + 4 * ty + a;
+        if (i >= T) continue;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) out[((size_t)i * kHQ + h) * kD + 4 * tx + b] = acc[a][b];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side: argument checks, launch plan, dispatch.
 // ---------------------------------------------------------------------------
 enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3 };
@@ -848,6 +968,50 @@ attn_status_t attn_prefill_splitkv(const void* q, const void* kCache, const void
     e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_merge_splits_kernel), dim3((C * kHQ + 3) / 4),
                         dim3(256), args, 0, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_naive_workspace(int T, size_t* bytes) {
+    if (!bytes) return ATTN_ERR_NULL_PTR;
+    if (T < 0 || T > 46340) return ATTN_ERR_INVALID_ARG;       // T*T fits int
+    *bytes = (size_t)kHQ * T * T * sizeof(float);
+    return ATTN_OK;
+}
+
+attn_status_t attn_naive(const float* q, const float* k, const float* v, float* out, int T, void* workspace,
+                         size_t workspaceBytes, hipStream_t stream) {
+    if (T < 0 || T > 46340) return ATTN_ERR_INVALID_ARG;
+    const attn_status_t st = attn_prefill_validate(q, k, v, out, T, 0, ATTN_DTYPE_F32);
+    if (st != ATTN_OK || T == 0) return st;
+    const size_t need = (size_t)kHQ * T * T * sizeof(float);
+    if (!workspace) return ATTN_ERR_NULL_PTR;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return ATTN_ERR_MISALIGNED;
+    if (workspaceBytes < need) return ATTN_ERR_WORKSPACE;
+    const size_t nq = (size_t)T * kHQ * kD * 4, nkv = (size_t)T * kHKV * kD * 4;
+    if (overlaps(workspace, need, q, nq) || overlaps(workspace, need, k, nkv) || overlaps(workspace, need, v, nkv) ||
+        overlaps(workspace, need, out, nq))
+        return ATTN_ERR_ALIAS;
+    float* S = static_cast<float*>(workspace);
+    const int nt = (T + kNT - 1) / kNT;
+    {
+        void* args[] = {&q, &k, &S, &T};
+        if (hipLaunchKernel(reinterpret_cast<const void*>(&naive_scores_kernel), dim3(nt, nt, kHQ), dim3(256), args,
+                            0, stream) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+    }
+    {
+        void* args[] = {&S, &T};
+        if (hipLaunchKernel(reinterpret_cast<const void*>(&naive_softmax_kernel), dim3(T, kHQ), dim3(256), args, 0,
+                            stream) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+    }
+    {
+        const float* Sc = S;
+        void* args[] = {&Sc, &v, &out, &T};
+        if (hipLaunchKernel(reinterpret_cast<const void*>(&naive_pv_kernel), dim3(nt, kHQ), dim3(256), args, 0,
+                            stream) != hipSuccess)
+            return ATTN_ERR_LAUNCH;
+    }
+    return ATTN_OK;
 }
 
 attn_status_t attn_prefill_rowwise(const void* q, const void* kCache, const void* vCache, float* out, int C, int P,

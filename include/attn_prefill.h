@@ -164,6 +164,28 @@ attn_status_t attn_prefill_splitkv(const void* q, const void* kCache, const void
  */
 attn_status_t attn_prefill_splitkv_workspace(int C, int P, attn_dtype_t dtype, size_t* bytes, int* splits);
 
+/*
+ * attn_naive -- causal prompt prefill (P = 0) by the three-kernel pipeline of
+ * "Inference Attention 1: The Full Score Matrix" (Lesson): a scores kernel
+ * writes the 32 x T x T fp32 score matrix (-inf above the diagonal) into
+ * `workspace`, a softmax kernel normalises each row in place, a weighted-sum
+ * kernel multiplies it by V.  A baseline that shows the memory cost the fused
+ * path removes; fp32 only.
+ *
+ *   q [T][32][64], k and v [T][8][64], out [T][32][64]: fp32 device memory as
+ *   for attn_prefill with C = T, P = 0
+ *   workspace       at least attn_naive_workspace(T) bytes (32*T*T floats),
+ *                   16-byte aligned, not overlapping any argument
+ *   T               prompt length, 0 <= T <= 46340
+ *
+ * Returns as attn_prefill; ATTN_ERR_WORKSPACE if the workspace is too small.
+ */
+attn_status_t attn_naive(const float* q, const float* k, const float* v, float* out, int T, void* workspace,
+                         size_t workspaceBytes, hipStream_t stream);
+
+/* Bytes of workspace attn_naive needs for T (32*T*T*4). Host-only. */
+attn_status_t attn_naive_workspace(int T, size_t* bytes);
+
 /* The argument checks of attn_prefill_paged alone; host-only, no HIP call. */
 attn_status_t attn_prefill_paged_validate(const void* q, const void* kPages, const void* vPages,
                                           const int* blockTable, int numBlocks, int pageSize, const float* out,

@@ -174,6 +174,26 @@ def test_splitkv_rejects_small_or_missing_workspace():
     assert lib.attn_prefill_splitkv(*args, A + 192 * MB, need, None) == ALIAS    # workspace on out
 
 
+def test_naive_workspace_and_rejections():
+    lib = cpf.load_library()
+    assert cpf.naive_workspace(0) == 0
+    assert cpf.naive_workspace(17) == 32 * 17 * 17 * 4
+    assert cpf.naive_workspace(2048) == 32 * 2048 * 2048 * 4 == 512 * MB
+    with pytest.raises(cpf.AttnError):
+        cpf.naive_workspace(-1)
+    with pytest.raises(cpf.AttnError):
+        cpf.naive_workspace(46341)
+    T = 100
+    need = cpf.naive_workspace(T)
+    args = (A, A + 64 * MB, A + 128 * MB, A + 192 * MB, T)
+    assert lib.attn_naive(*args, A + 256 * MB, need - 4, None) == WORKSPACE
+    assert lib.attn_naive(*args, None, need, None) == NULLP
+    assert lib.attn_naive(*args, A + 256 * MB + 4, need, None) == MISAL
+    assert lib.attn_naive(*args, A + 128 * MB, need, None) == ALIAS       # workspace on v
+    assert lib.attn_naive(A, A + 64 * MB, A + 128 * MB, A + 192 * MB, -1, A + 256 * MB, need, None) == 1
+    assert lib.attn_naive(None, None, None, None, 0, None, 0, None) == 0  # T = 0 is a no-op
+
+
 def test_plan_errors():
     with pytest.raises(cpf.AttnError):
         cpf.plan(-1, 0)
