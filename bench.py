@@ -288,8 +288,9 @@ def main():
         # decode is bandwidth-bound: roofline against HBM on the compulsory bytes
         gbs = alg_bytes / (kernel_ms * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                              "kernel": "attn_prefill_kernel (split) + attn_merge_splits_kernel",
+                              "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_entry(name),
+                              "kernel": ("attn_decode_split_kernel" if C == 1 and dt == "f32" else
+                                         "attn_prefill_kernel (split)") + " + attn_merge_splits_kernel",
                               "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": alg_bytes}
     if not args.no_speedup and not paged and not splitkv:
         # the per-row starter algorithm on the same inputs, same run: the page's SPEEDUP

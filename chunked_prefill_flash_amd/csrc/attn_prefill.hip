@@ -67,6 +67,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 template <typename T> struct Elem;
@@ -119,9 +120,18 @@ __device__ __forceinline__ int chunk_code(int r) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xchg_half(float x) {
-    // value of the lane 32 positions away (the other half-wave)
-    return __shfl_xor(x, 32, 64);
+// Lanes n and n+32 of a wave hold different keys of the same query.  One
+// v_permlane32_swap with x in both operands (it exchanges the upper half of
+// the first with the lower half of the second) leaves, in every lane, the
+// lower half's x of that query in one result and the upper half's in the
+// other, so both lanes combine the same two values and agree bitwise.
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -168,6 +178,12 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps load descriptors scalar
     const int wr = wid % NW;   // row sub-tile of this wave
     const int wp = wid / NW;   // key split of this wave
+    if constexpr (sizeof(T) == 2) {
+        // bf16 is bound by the softmax arithmetic: waves of even key split win
+        // issue ties, so the two waves sharing a SIMD drift out of phase and
+        // one's exponentials overlap the other's MFMAs
+        if ((wp & 1) == 0) __builtin_amdgcn_s_setprio(1);
+    }
     const int n = lane & 31;   // query slot
     const int hh = lane >> 5;  // half-wave
     const int g = blockIdx.x % kHKV;
@@ -358,7 +374,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             float bm = s[0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) bm = fmaxf(bm, s[r]);
-            bm = fmaxf(bm, xchg_half(bm));
+            bm = half_max(bm);
             if constexpr (!kF32) bm *= kScaleLog2;      // bf16 scores are raw dot products
             const bool upd = bm > m + kRescaleSlack;
             if (__ballot(upd)) {
@@ -373,16 +389,18 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             }
             const float mu = m == -INFINITY ? 0.f : m;
             float p[16];
-            float ps = 0.f;
+            if constexpr (kF32) {
+                float ps = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                if constexpr (kF32)
+                for (int r = 0; r < 16; ++r) {
                     p[r] = fast_exp2(s[r] - mu);
-                else
-                    p[r] = fast_exp2(__builtin_fmaf(s[r], kScaleLog2, -mu));
-                ps += p[r];
+                    ps += p[r];
+                }
+                l += ps;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], kScaleLog2, -mu));
             }
-            l += ps;
             if constexpr (kF32) {
                 // key 8(t/4) + 4hh + t%4 of the sub-block: V[key][n] and V[key][n+32]
 #pragma unroll
@@ -400,6 +418,11 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     bf8 pb;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[8 * u + e];
+                    // the denominator sums the same rounded weights the PV product uses
+                    constexpr bf2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2)
+                        l = __builtin_amdgcn_fdot2_f32_bf16(bf2{pb[e], pb[e + 1]}, kOnes, l, false);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt) {
                         const unsigned char* a = Vs + 16 * u * kRB + voff[nt];
@@ -500,7 +523,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         if constexpr (SPLIT) {
             // key split: unnormalised partial O, running max m and denominator l
             if (wp == 0 && wave_active && row < C) {
-                const float lt = l + xchg_half(l);
+                const float lt = half_sum(l);
                 const size_t qi = ((size_t)split * C + row) * kHQ + head;
                 float* dst = ks.part + qi * kD + 4 * hh;
 #pragma unroll
@@ -513,12 +536,10 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     ml[0] = m;
                     ml[1] = lt;
                 }
-            } else if (wp == 0 && wave_active) {
-                (void)xchg_half(l);                 // keep the half-wave exchange uniform
             }
         } else if (wp == 0 && wave_active) {
             (void)ks;
-            const float lt = l + xchg_half(l);
+            const float lt = half_sum(l);
             const float inv = 1.0f / lt;
             if (row < C) {
                 float* dst = out + ((size_t)row * kHQ + head) * kD + 4 * hh;
@@ -611,42 +632,212 @@ __device__ __forceinline__ float wave_sum64(float x) {
 
 __global__ void __launch_bounds__(256)
 attn_merge_splits_kernel(const float* __restrict__ part, float* __restrict__ out, int C, int P, int len, int n) {
-    const int qi = blockIdx.x * 4 + (threadIdx.x >> 6);    // (row, head) index
+    // (row, head) index, wave-uniform: split offsets below stay scalar
+    const int qi = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (qi >= C * kHQ) return;                           // whole waves leave together
     const int row = qi / kHQ;
     const int lane = threadIdx.x & 63;                   // output dim; also a split index below
     const int ns = min(n, (P + row) / len + 1);
     const float* ml = part + (size_t)n * C * kHQ * kD;
     const size_t stride = (size_t)C * kHQ;              // between splits, in (row, head) units
-    // split maxima, 64 splits at a time (one per lane)
-    float mx = -INFINITY;
+    // 64 splits at a time, all their loads issued together (indices clamped
+    // into range; the weight of a clamped slot is 0), combined online
+    float M = -INFINITY, L = 0.f, O = 0.f;
     for (int s0 = 0; s0 < ns; s0 += 64) {
-        const int s = s0 + lane;
-        if (s < ns) mx = fmaxf(mx, ml[(s * stride + qi) * 2]);
-    }
-    mx = wave_max64(mx);
-    float L = 0.f, O = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 64) {
-        const int s = s0 + lane;
-        float w = 0.f, wl = 0.f;
-        if (s < ns) {
-            w = fast_exp2(ml[(s * stride + qi) * 2] - mx);
-            wl = w * ml[(s * stride + qi) * 2 + 1];
-        }
-        L += wave_sum64(wl);
         const int cnt = min(64, ns - s0);
+        const int sl = s0 + min(lane, cnt - 1);
+        const float ms = ml[(sl * stride + qi) * 2];
+        const float ls = ml[(sl * stride + qi) * 2 + 1];
         const float* src = part + ((size_t)s0 * stride + qi) * kD + lane;
-        int t = 0;
-        for (; t + 8 <= cnt; t += 8) {                   // eight independent loads in flight
-            float x[8];
+        float x[64];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) x[u] = src[(size_t)(t + u) * stride * kD];
+        for (int t = 0; t < 64; ++t) x[t] = src[(size_t)min(t, cnt - 1) * stride * kD];
+        const float mc = wave_max64(lane < cnt ? ms : -INFINITY);
+        const float mn = fmaxf(M, mc);                   // finite: every reached split saw a key
+        const float scale = fast_exp2(M - mn);           // 0 on the first chunk
+        const float w = lane < cnt ? fast_exp2(ms - mn) : 0.f;
+        L = L * scale + wave_sum64(w * ls);
+        float acc = 0.f;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) O += __shfl(w, t + u, 64) * x[u];
-        }
-        for (; t < cnt; ++t) O += __shfl(w, t, 64) * src[(size_t)t * stride * kD];
+        for (int t = 0; t < 64; ++t)
+            acc = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), t)), x[t], acc);
+        O = O * scale + acc;
+        M = mn;
     }
     out[(size_t)qi * kD + lane] = O / L;
+}
+
+// ---------------------------------------------------------------------------
+// Single fp32 token (C = 1) for the split-KV entry point ("FlashAttention and
+// inference kernels", Flash-Decoding: split the key range, one partial
+// (O, m, l) per split, merged afterwards).  One token leaves 31 of the 32
+// query slots of an MFMA tile empty, and fp32 MFMAs cost as much time as the
+// loads here, so this kernel uses plain FMAs instead:
+// lane = 8 * key slot + dim slice; the 8 lanes of a key slot each hold 8 dims
+// of q (4 heads of the group) and of the key's K and V rows.  Every key slot
+// runs its own online softmax over the keys it visits (no cross-lane traffic
+// in the loop beyond the 3-step sum of the dot products); the slots, then the
+// waves, are merged at the end by the log-sum-exp rule.  Partials use the
+// layout and log2 units of the MFMA split kernel, so the same merge kernel
+// finishes the job.
+// ---------------------------------------------------------------------------
+constexpr int kDecWaves = 4;        // waves per workgroup
+constexpr int kDecUnroll = 4;       // key chunks (8 keys per wave) loaded together
+constexpr float kDecFloor = -1e30f; // running-max start: finite, below any score
+
+__device__ __forceinline__ void load_row8(const float* p, float (&x)[8]) {
+    const f4 a = *reinterpret_cast<const f4*>(p);
+    const f4 b = *reinterpret_cast<const f4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[e] = a[e];
+        x[4 + e] = b[e];
+    }
+}
+
+// sum over the 8 consecutive lanes of a key slot; every lane ends with the
+// same bits (each step adds the same two values in either order)
+__device__ __forceinline__ float slot_sum8(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // 7 - lane
+    return x;
+}
+
+__global__ void __launch_bounds__(64 * kDecWaves)
+attn_decode_split_kernel(const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
+                         float* __restrict__ part, int P, int len, int n) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slot = lane >> 3;         // key slot 0..7
+    const int ds = lane & 7;            // dims 8*ds .. 8*ds+7
+    const int g = blockIdx.x % kHKV;
+    const int split = blockIdx.x / kHKV;
+    const int total = P + 1;
+    const int kbeg = split * len;
+    const int kend = min(total, kbeg + len);
+
+    float qf[4][8];                     // q of heads 4g..4g+3, scaled by log2(e)/8
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        load_row8(q + (size_t)(kGroup * g + h) * kD + 8 * ds, qf[h]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[h][e] *= kScaleLog2;
+    }
+    float m[4], l[4], acc[4][8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        m[h] = kDecFloor;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    }
+
+    constexpr int kStep = 8 * kDecWaves;    // keys between a wave's consecutive chunks
+    for (int c0 = kbeg + 8 * w; c0 < kend; c0 += kStep * kDecUnroll) {
+        float kx[kDecUnroll][8], vx[kDecUnroll][8];
+        bool ok[kDecUnroll];
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+            const int key = c0 + kStep * u + slot;
+            ok[u] = key < kend;
+            const size_t off = ((size_t)(ok[u] ? key : kbeg) * kHKV + g) * kD + 8 * ds;   // in range either way
+            load_row8(kc + off, kx[u]);
+            load_row8(vc + off, vx[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qf[h][e], kx[u][e], d);
+                d = slot_sum8(d);
+                const float sv = ok[u] ? d : -INFINITY;
+                if (sv > m[h] + kRescaleSlack) {    // rare after the first keys
+                    const float alpha = fast_exp2(m[h] - sv);
+                    m[h] = sv;
+                    l[h] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+                }
+                const float pr = fast_exp2(sv - m[h]);   // 0 for a key past the range
+                l[h] += pr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(pr, vx[u][e], acc[h][e]);
+            }
+        }
+    }
+
+    // merge the 8 key slots of the wave (lanes 8 apart hold the same dims):
+    // slots 8 apart by a DPP rotate within 16-lane rows, then rows and halves
+    // by permlane swaps; every step combines the same two partials in both
+    // lanes, in either order
+    auto merge_with = [&](auto other) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            float m0, m1, l0, l1;
+            other(m[h], m0, m1);
+            other(l[h], l0, l1);
+            const float mm = fmaxf(m0, m1);
+            const float a = fast_exp2(m0 - mm), b = fast_exp2(m1 - mm);
+            l[h] = a * l0 + b * l1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x0, x1;
+                other(acc[h][e], x0, x1);
+                acc[h][e] = a * x0 + b * x1;
+            }
+            m[h] = mm;
+        }
+    };
+    merge_with([](float x, float& a, float& b) {
+        a = x;
+        b = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));   // row_ror 8
+    });
+    merge_with([](float x, float& a, float& b) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    });
+    merge_with([](float x, float& a, float& b) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    });
+    // merge the waves through LDS: per wave and head, 64 dims + m + l
+    __shared__ float sm[kDecWaves][4][kD + 2];
+    if (slot == 0) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm[w][h][8 * ds + e] = acc[h][e];
+            if (ds == 0) {
+                sm[w][h][kD] = m[h];
+                sm[w][h][kD + 1] = l[h];
+            }
+        }
+    }
+    __syncthreads();
+    const int h = tid >> 6, d = tid & 63;   // 256 threads = 4 heads x 64 dims
+    float mm = sm[0][h][kD];
+#pragma unroll
+    for (int v = 1; v < kDecWaves; ++v) mm = fmaxf(mm, sm[v][h][kD]);
+    float O = 0.f, L = 0.f;
+#pragma unroll
+    for (int v = 0; v < kDecWaves; ++v) {
+        const float wt = fast_exp2(sm[v][h][kD] - mm);
+        O += wt * sm[v][h][d];
+        L += wt * sm[v][h][kD + 1];
+    }
+    const size_t qi = (size_t)split * kHQ + kGroup * g + h;   // C = 1: (split, row 0, head)
+    part[qi * kD + d] = O;
+    if (d == 0) {
+        float* ml = part + (size_t)n * kHQ * kD + qi * 2;
+        ml[0] = mm;
+        ml[1] = L;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -772,7 +963,7 @@ naive_pv_kernel(const float* __restrict__ S, const float* __restrict__ v, float*
 // ---------------------------------------------------------------------------
 // Host side: argument checks, launch plan, dispatch.
 // ---------------------------------------------------------------------------
-enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3 };
+enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3, kV_decode = 4 };
 
 struct Plan {
     int rows, ks, grid, threads, per_wg, bk, lds, variant, n_row_tiles, paired;
@@ -847,6 +1038,29 @@ hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, 
 // split then streams more tiles), each split at least two staged tiles long;
 // split length a multiple of the staged tile.
 Plan split_plan(int C, int P, attn_dtype_t dtype) {
+    if (C == 1 && dtype == ATTN_DTYPE_F32) {
+        // one fp32 token: the FMA decode kernel, splits of a multiple of 64
+        // keys, at most 32 of them (up to 256 four-wave workgroups; measured
+        // faster than 16, 24, 64 or 128 at 16384 keys).  bf16 stays on the MFMA
+        // kernel below: with twice the keys per byte the FMA work is no longer
+        // hidden behind the loads, and bf16 MFMAs are cheap enough.
+        Plan p{};
+        const int total = P + 1;
+        int len = (total + 31) / 32;
+        len = max(64, (len + 63) / 64 * 64);
+        p.rows = 1;
+        p.ks = kDecWaves;
+        p.threads = 64 * kDecWaves;
+        p.bk = 8;
+        p.lds = kDecWaves * 4 * (kD + 2) * 4;
+        p.variant = kV_decode;
+        p.n_row_tiles = 1;
+        p.per_wg = 1;
+        p.split_len = len;
+        p.splits = (total + len - 1) / len;
+        p.grid = kHKV * p.splits;
+        return p;
+    }
     // short chunks: 8-row work items; longer ones: 16 rows (both 4 key-split waves)
     Plan p = C < 256 ? (dtype == ATTN_DTYPE_BF16 ? make_plan<__bf16, 1, 4>(C, kV_1x4) : make_plan<float, 1, 4>(C, kV_1x4))
                      : (dtype == ATTN_DTYPE_BF16 ? make_plan<__bf16, 2, 4>(C, kV_2x4) : make_plan<float, 2, 4>(C, kV_2x4));
@@ -958,12 +1172,20 @@ attn_status_t attn_prefill_splitkv(const void* q, const void* kCache, const void
         return ATTN_ERR_ALIAS;
     const PagedCache none{nullptr, 1, 0};
     const KeySplit ksp{static_cast<float*>(workspace), p.split_len, p.splits};
-    hipError_t e = dtype == ATTN_DTYPE_BF16
-                       ? dispatch<__bf16, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream)
-                       : dispatch<float, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream);
+    int len = p.split_len, n = p.splits;
+    hipError_t e;
+    if (p.variant == kV_decode) {
+        float* wsp = static_cast<float*>(workspace);
+        void* dargs[] = {const_cast<void**>(&q), const_cast<void**>(&kCache), const_cast<void**>(&vCache), &wsp, &P,
+                         &len, &n};
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_decode_split_kernel), dim3(p.grid), dim3(p.threads),
+                            dargs, 0, stream);
+    } else {
+        e = dtype == ATTN_DTYPE_BF16 ? dispatch<__bf16, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream)
+                                     : dispatch<float, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream);
+    }
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
     const float* part = static_cast<const float*>(workspace);
-    int len = p.split_len, n = p.splits;
     void* args[] = {&part, &out, &C, &P, &len, &n};
     e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_merge_splits_kernel), dim3((C * kHQ + 3) / 4),
                         dim3(256), args, 0, stream);

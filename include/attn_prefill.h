@@ -140,7 +140,9 @@ attn_status_t attn_prefill_rowwise(const void* q, const void* kCache, const void
  * partial (O_s, m_s, l_s) per (row, head) to `workspace`, and a second kernel
  * merges them with weights e^(m_s - m) over the splits each row reaches.  For
  * short chunks (decode, C = 1..64) against long prefixes, where row tiles x KV
- * groups alone cannot fill the GPU.
+ * groups alone cannot fill the GPU.  A single fp32 token (C = 1) is split by
+ * a kernel built on plain FMAs (no MFMA tile to fill); everything else uses
+ * the tiled MFMA kernel with a key range per workgroup.
  *
  *   workspace       device memory of at least attn_prefill_splitkv_workspace()
  *                   bytes, 16-byte aligned, not overlapping any argument;

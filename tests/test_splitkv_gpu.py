@@ -89,3 +89,42 @@ def test_splitkv_matches_single_pass():
     got, _ = run(q, k, v, P)
     one = cpf.attn_prefill(gpu(q), gpu(k), gpu(v), P=P).cpu().numpy()
     assert np.max(np.abs(got - one)) < 1e-5
+
+
+@pytest.mark.parametrize("P", [0, 7, 8, 62, 63, 64, 65, 511, 4095, 100000])
+def test_decode_one_token_fp32(P):
+    """One token (the FMA decode kernel): split edges at multiples of 64 keys,
+    waves and key slots with no keys, and a cache longer than 64 splits'
+    worth of the minimum split."""
+    q, k, v = synth.case_plain(1, P, 7500 + P)
+    got, splits = run(q, k, v, P)
+    close_f32(got, oracle.attn_prefill(q, k, v, P))
+    assert 1 <= splits <= 32
+
+
+@pytest.mark.parametrize("P", [5, 1000, 50000])
+def test_decode_one_token_bf16(P):
+    q, k, v = synth.case_plain(1, P, 7600 + P)
+    got, _ = run(q, k, v, P, "bf16")
+    qo, ko, vo = widen(q), widen(k), widen(v)
+    ref = oracle.attn_prefill(qo, ko, vo, P)
+    a = oracle.attn_prefill(qo, ko, np.abs(vo), P)
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= 1e-5 + 2.0 ** -8 * a)
+
+
+def test_decode_planted_maximum_in_last_split():
+    """The row's dominant key is its last one (the token itself), so the
+    running maximum jumps in the last split and the merge must rescale."""
+    P = 20000
+    q, k, v, pos = synth.case_last_key(1, P, 7700)
+    got, splits = run(q, k, v, P)
+    assert splits > 1 and pos == [P]
+    assert np.all(got[0, 0] == np.float32(4.0))
+    close_f32(got, oracle.attn_prefill(q, k, v, P))
+
+
+def test_decode_deterministic():
+    q, k, v = synth.case_plain(1, 9999, 7800)
+    a, _ = run(q, k, v, 9999)
+    b, _ = run(q, k, v, 9999)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
