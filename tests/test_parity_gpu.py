@@ -7,9 +7,10 @@ Lesson: every value checked against double sums at 1e-4 plus 1e-3 relative):
                 on the bf16-rounded inputs and A = sum_j w_j |V_j| (the oracle
                 run on |V|).  Scores of bf16 inputs are exact products summed
                 in fp32; the one bf16-specific rounding is that of each
-                probability to bf16 before the PV product (relative <= 2^-9),
-                which moves the output by at most 2^-9 * A.  The bound allows
-                twice that.
+                probability to bf16 before the PV product (relative <= 2^-9).
+                The kernel sums its denominator from the same rounded weights,
+                so each normalised weight moves by at most twice that relative
+                amount (to first order) and the output by at most 2^-8 * A.
 A NaN or inf anywhere fails.  The output is poisoned with quiet NaN before
 each call and surrounded by canary guard bands that must survive.
 """
