@@ -217,15 +217,33 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     const int rl = lane / kCPR;                     // row within one load
     const int pc = lane % kCPR;                     // chunk position within the row
     auto load_row = [&](int u) { return ((wid + u * G::kWaves) % (kBK / kRPL)) * kRPL + rl; };
-    // physical page of each of this lane's load rows in tile t (paged cache only)
-    auto lookup_pages = [&](int t, int (&phys)[kLPW]) {
-#pragma unroll
-        for (int u = 0; u < kLPW; ++u) {
-            const int key = kb + t * kBK + load_row(u);
-            phys[u] = key < total ? pg.table[key / pg.page_size] : -1;
-        }
+    // Paged cache: the byte offset of every K/V row of tile t sits in LDS slot
+    // t & 1, written two tiles ahead by the first kBK threads (one table read
+    // each, in flight during a tile's math), so a lane holds no page state.
+    __shared__ uint32_t pofs[PAGED ? 2 * kBK : 1];
+    constexpr uint32_t kNoRow = 0xffffffffu;        // past the cache, or a bad table entry
+    struct PageRef {
+        int ph;     // table entry (-1 past the cache)
+        int slot;   // position within the page
     };
-    auto issue_tile = [&](int t, unsigned char* stage, const int (&phys)[kLPW]) {
+    auto fetch_page = [&](int t) {                  // key kb + t*kBK + tid; divides before the tile's math
+        const int key = kb + t * kBK + tid;
+        PageRef r{-1, 0};
+        if (tid < kBK && key < total) {
+            const int blk = key / pg.page_size;
+            r.slot = key - blk * pg.page_size;
+            r.ph = pg.table[blk];
+        }
+        return r;
+    };
+    auto store_offset = [&](int t, PageRef r) {
+        if (tid < kBK)
+            pofs[(t & 1) * kBK + tid] =
+                r.ph >= 0 && r.ph < pg.num_blocks
+                    ? (uint32_t)(((size_t)r.ph * pg.page_size + r.slot) * kHKV + g) * kRB
+                    : kNoRow;
+    };
+    auto issue_tile = [&](int t, unsigned char* stage) {
         const int key0 = kb + t * kBK;
         uint32_t range;
         size_t base;
@@ -247,11 +265,8 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             const int lc = pc ^ chunk_code<T>(row);     // logical chunk stored at position pc
             uint32_t voff;
             if constexpr (PAGED) {
-                const int key = key0 + row;
-                const int ph = phys[u];
-                voff = (ph >= 0 && ph < pg.num_blocks)
-                           ? (uint32_t)(((size_t)ph * pg.page_size + key % pg.page_size) * kHKV + g) * kRB + lc * 16
-                           : range;
+                const uint32_t ro = pofs[(t & 1) * kBK + row];
+                voff = ro == kNoRow ? range : ro + lc * 16;   // ro + lc*16 < range for a valid row
             } else {
                 voff = (uint32_t)(row * kHKV + g) * kRB + lc * 16;
             }
@@ -276,12 +291,14 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         const int head = g * kGroup + (n & 3);
         const int lim = P + row;                    // this lane's query sees keys <= lim
 
-        int physA[kLPW], physB[kLPW];   // page lookups, two tiles ahead (paged cache)
-        if constexpr (PAGED) lookup_pages(0, physA);
-        issue_tile(0, stage0, physA);
         if constexpr (PAGED) {
-            if (ntiles > 1) lookup_pages(1, physB);
+            const PageRef ph0 = fetch_page(0);
+            const PageRef ph1 = ntiles > 1 ? fetch_page(1) : PageRef{-1, 0};
+            store_offset(0, ph0);
+            if (ntiles > 1) store_offset(1, ph1);
+            __syncthreads();
         }
+        issue_tile(0, stage0);
 
         // ---- Q operand (B of S^T = K Q^T), held for the whole key loop ----
         // fp32: qf[s] = q[row][head][32*hh + s] * log2(e)/8, s = 0..31
@@ -462,25 +479,31 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // stage was last read before the previous barrier.
         __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile 0 has landed in LDS
         __syncthreads();
+        // Paged: the table entries of tile t+2 are read during tile t and their
+        // offsets stored after its vmcnt(0), into the slot tile t's loads used
+        // (every wave issued those before the previous barrier).
         for (int t = 0; t < ntiles; t += 2) {
-            if (t + 1 < ntiles) {
-                issue_tile(t + 1, stage1, physB);
-                if constexpr (PAGED) {
-                    if (t + 2 < ntiles) lookup_pages(t + 2, physA);
-                }
+            PageRef ph{-1, 0};
+            if (t + 1 < ntiles) issue_tile(t + 1, stage1);
+            if constexpr (PAGED) {
+                if (t + 2 < ntiles) ph = fetch_page(t + 2);
             }
             consume(std::integral_constant<int, 0>{}, t);
             __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile t+1 has landed
+            if constexpr (PAGED) {
+                if (t + 2 < ntiles) store_offset(t + 2, ph);
+            }
             __syncthreads();
             if (t + 1 < ntiles) {
-                if (t + 2 < ntiles) {
-                    issue_tile(t + 2, stage0, physA);
-                    if constexpr (PAGED) {
-                        if (t + 3 < ntiles) lookup_pages(t + 3, physB);
-                    }
+                if (t + 2 < ntiles) issue_tile(t + 2, stage0);
+                if constexpr (PAGED) {
+                    if (t + 3 < ntiles) ph = fetch_page(t + 3);
                 }
                 consume(std::integral_constant<int, G::kStageBytes>{}, t + 1);
                 __builtin_amdgcn_s_waitcnt(0x3f70);
+                if constexpr (PAGED) {
+                    if (t + 3 < ntiles) store_offset(t + 3, ph);
+                }
                 __syncthreads();
             }
         }
@@ -995,11 +1018,13 @@ Plan make_plan(int C, int variant) {
 // 4 key splits.  Short chunks: 8 rows, 4 key splits.
 template <typename T>
 Plan choose_plan(int C, bool paged) {
-    // (the paged fp32 16-wave kernel would spill at 128 VGPRs; it uses 8 waves)
-    if (C >= 1024)
-        return sizeof(T) == 4 && !paged ? make_plan<T, 4, 4>(C, kV_4x4) : make_plan<T, 4, 2>(C, kV_4x2);
-    if (C >= 256) return make_plan<T, 2, 4>(C, kV_2x4);
-    return make_plan<T, 1, 4>(C, kV_1x4);
+    // (the paged fp32 16-wave kernel spills at 128 VGPRs and gains only ~1%; it
+    // uses 8 waves)
+    Plan p = C >= 1024 ? (sizeof(T) == 4 && !paged ? make_plan<T, 4, 4>(C, kV_4x4) : make_plan<T, 4, 2>(C, kV_4x2))
+             : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4)
+                        : make_plan<T, 1, 4>(C, kV_1x4);
+    p.lds += 4 * (paged ? 2 * p.bk : 1);   // the page-offset table (one word when unused)
+    return p;
 }
 
 Plan plan_for(int C, attn_dtype_t dtype, bool paged) {
@@ -1066,6 +1091,7 @@ Plan split_plan(int C, int P, attn_dtype_t dtype) {
                      : (dtype == ATTN_DTYPE_BF16 ? make_plan<__bf16, 2, 4>(C, kV_2x4) : make_plan<float, 2, 4>(C, kV_2x4));
     p.paired = 0;
     p.per_wg = 1;
+    p.lds += 4;   // the unused page-offset word
     const int total = P + C;
     const int base = p.n_row_tiles * kHKV;
     constexpr int kTargetWorkgroups = 256;

@@ -91,7 +91,9 @@ def test_paged_equals_contiguous_bitwise():
     C, P = 600, 1000
     q, k, v = synth.case_plain(C, P, 5400)
     kp, vp, table = synth.to_pages(k, v, 16, 5401)
-    assert cpf.plan(C, P, paged=True) == cpf.plan(C, P)
+    pp, pc = cpf.plan(C, P, paged=True), cpf.plan(C, P)
+    assert pp.pop("lds_bytes") == pc.pop("lds_bytes") - 4 + 2 * 4 * pc["keys_per_tile"]   # + page-offset table
+    assert pp == pc
     paged = run_paged(q, kp, vp, table, P, "f32")
     contig = cpf.attn_prefill(to_gpu(q, "f32"), to_gpu(k, "f32"), to_gpu(v, "f32"), P=P).cpu().numpy()
     assert np.array_equal(paged.view(np.uint32), contig.view(np.uint32))
