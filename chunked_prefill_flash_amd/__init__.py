@@ -21,8 +21,9 @@ import os
 import torch  # imported first so the library binds to torch's HIP runtime
 
 __all__ = ["attn_prefill", "attn_prefill_paged", "attn_prefill_rowwise", "attn_prefill_splitkv",
-           "splitkv_workspace", "attn_naive", "naive_workspace", "validate", "paged_validate", "plan", "status_string", "library_path", "load_library",
-           "flops", "visible_pairs", "AttnError", "EXPORTED_SYMBOLS", "HQ", "HKV", "D"]
+           "splitkv_workspace", "attn_naive", "naive_workspace", "validate", "paged_validate", "plan",
+           "status_string", "library_path", "load_library", "flops", "visible_pairs", "AttnError",
+           "EXPORTED_SYMBOLS", "HQ", "HKV", "D"]
 
 HQ, HKV, D = 32, 8, 64
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -79,17 +80,50 @@ def load_library():
     lib.attn_prefill_validate.argtypes = [vp, vp, vp, vp, i, i, i]
     lib.attn_prefill_validate.restype = i
     lib.attn_prefill_plan.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_int)]
+    lib.attn_prefill_plan.restype = i
     lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, i, i, vp, i, i, i, vp]
     lib.attn_prefill_paged.restype = i
     lib.attn_prefill_paged_validate.argtypes = [vp, vp, vp, vp, i, i, vp, i, i, i]
     lib.attn_prefill_paged_validate.restype = i
-    lib.attn_prefill_plan.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_prefill_version.argtypes = []
     lib.attn_prefill_version.restype = i
     _lib = lib
     return lib
+
+
+def _gpu_tensors(device, **tensors):
+    """Every tensor contiguous and on `device` (a GPU)."""
+    for name, t in tensors.items():
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+        if t.device != device:
+            raise ValueError("%s is on %s, expected %s (all tensors on one device)" % (name, t.device, device))
+
+
+def _out_tensor(out, C: int, device) -> torch.Tensor:
+    """The caller's out (checked) or a new float32 [C][32][64] on `device`."""
+    if out is None:
+        return torch.empty((C, HQ, D), dtype=torch.float32, device=device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (C, HQ, D):
+        raise ValueError("out must be float32 [C][32][64] = [%d][32][64], got %s %s"
+                         % (C, out.dtype, tuple(out.shape)))
+    _gpu_tensors(device, out=out)
+    return out
+
+
+def _workspace(workspace, need: int, device) -> torch.Tensor:
+    """The caller's workspace (checked for device and contiguity; the library
+    checks its size) or a new one of `need` bytes."""
+    if workspace is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    _gpu_tensors(device, workspace=workspace)
+    return workspace
+
+
+def _stream(stream, device):
+    return stream if stream is not None else torch.cuda.current_stream(device)
 
 
 def status_string(code: int) -> str:
@@ -149,16 +183,9 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
     if k.shape != (P + C, HKV, D) or v.shape != k.shape:
         raise ValueError("k and v must be [P+C][8][64] = [%d][8][64], got %s and %s"
                          % (P + C, tuple(k.shape), tuple(v.shape)))
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("%s must be a contiguous GPU tensor" % name)
-    if out is None:
-        out = torch.empty((C, HQ, D), dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or out.shape != (C, HQ, D) or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError("out must be a contiguous float32 GPU tensor [C][32][64]")
-    if len({q.device, k.device, v.device, out.device}) != 1:
-        raise ValueError("all tensors must be on one device")
-    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    _gpu_tensors(q.device, q=q, k=k, v=v)
+    out = _out_tensor(out, C, q.device)
+    s = _stream(stream, q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = getattr(lib, _entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), C, P, DTYPES[q.dtype],
@@ -196,14 +223,9 @@ def attn_prefill_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
     if block_table.dtype != torch.int32 or block_table.dim() != 1 or \
             block_table.shape[0] < -(-(P + C) // page_size):
         raise ValueError("block_table must be int32 with at least ceil((P+C)/pageSize) entries")
-    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("%s must be a contiguous GPU tensor" % name)
-    if out is None:
-        out = torch.empty((C, HQ, D), dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or out.shape != (C, HQ, D) or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError("out must be a contiguous float32 GPU tensor [C][32][64]")
-    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    _gpu_tensors(q.device, q=q, k_pages=k_pages, v_pages=v_pages, block_table=block_table)
+    out = _out_tensor(out, C, q.device)
+    s = _stream(stream, q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.attn_prefill_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
@@ -238,20 +260,11 @@ def attn_prefill_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out:
         P = k.shape[0] - C
     if q.dim() != 3 or q.shape[1:] != (HQ, D) or k.shape != (P + C, HKV, D) or v.shape != k.shape:
         raise ValueError("bad shapes q %s k %s v %s for P=%d" % (tuple(q.shape), tuple(k.shape), tuple(v.shape), P))
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("%s must be a contiguous GPU tensor" % name)
-    if out is None:
-        out = torch.empty((C, HQ, D), dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or out.shape != (C, HQ, D) or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError("out must be a contiguous float32 GPU tensor [C][32][64]")
-    need, _ = splitkv_workspace(C, P, q.dtype)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous GPU tensor")
+    _gpu_tensors(q.device, q=q, k=k, v=v)
+    out = _out_tensor(out, C, q.device)
+    workspace = _workspace(workspace, splitkv_workspace(C, P, q.dtype)[0], q.device)
     nbytes = workspace.numel() * workspace.element_size()
-    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    s = _stream(stream, q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.attn_prefill_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), C, P, DTYPES[q.dtype],
@@ -279,16 +292,11 @@ def attn_naive(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Ten
     T = q.shape[0]
     if q.shape != (T, HQ, D) or k.shape != (T, HKV, D) or v.shape != k.shape:
         raise ValueError("q [T][32][64], k and v [T][8][64] expected")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("%s must be a contiguous GPU tensor" % name)
-    if out is None:
-        out = torch.empty((T, HQ, D), dtype=torch.float32, device=q.device)
-    need = naive_workspace(T)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _gpu_tensors(q.device, q=q, k=k, v=v)
+    out = _out_tensor(out, T, q.device)
+    workspace = _workspace(workspace, naive_workspace(T), q.device)
     nbytes = workspace.numel() * workspace.element_size()
-    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    s = _stream(stream, q.device)
     with torch.cuda.device(q.device):
         st = load_library().attn_naive(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), T,
                                        workspace.data_ptr(), nbytes, s.cuda_stream)

@@ -29,21 +29,27 @@
 //   so the probabilities feed the B operand straight from the score
 //   registers (the key order inside a sub-block is free because PV sums over
 //   keys; V is read in the matching order).
-// * K/V tiles are staged in LDS with padded rows so the MFMA operand reads are
-//   free of bank conflicts; the next tile's global loads are issued before the
-//   current tile's math and written to the other LDS buffer after it.
+// * K/V tiles go from HBM straight into LDS (bounds-checked buffer loads with
+//   an LDS destination), rows unpadded with their 16-byte chunks XOR-permuted
+//   per row so the MFMA operand reads avoid bank conflicts; the next tile's
+//   loads are in flight while the current tile is consumed (two stages).
 // * A workgroup is NW row-waves x KS key-split waves.  Key-split waves take
 //   alternate 32-key sub-blocks of each tile and are merged once at the end
 //   with the log-sum-exp rule ("FlashAttention and inference kernels",
 //   Flash-Decoding section and Exercises, exercise 2), skipping empty splits.
 // * blockIdx.x % 8 selects the KV group: consecutive workgroups go to the 8
 //   XCDs round-robin, so every XCD's L2 holds the K/V of one group only.
-// * Rows tiles i and n-1-i can be paired in one workgroup so every workgroup
+// * Row tiles i and n-1-i can be paired in one workgroup so every workgroup
 //   does the same causal work.
 // * exp is evaluated as exp2 with log2(e)/8 folded in (into Q for fp32, into an
-//   FMA for bf16).  The running maximum is only moved when a tile's maximum
-//   exceeds it by more than 2^8 (log2 units); any reference value gives the
-//   same softmax because it cancels in O/l, and p stays <= 256.
+//   FMA for bf16).  The running maximum is only moved when a sub-block's
+//   maximum exceeds it by more than 8 in log2 units; any reference value gives
+//   the same softmax because it cancels in O/l, and p stays <= 2^8.
+//
+// Other kernels in this file: the same kernel in paged-cache and key-split
+// modes, an FMA kernel for one fp32 decode token, the merge of key-split
+// partials, and two baselines timed against the fused kernel (the per-row
+// starter algorithm and the three-kernel pipeline with the full score matrix).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <limits.h>
@@ -134,9 +140,6 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// ---------------------------------------------------------------------------
-// The kernel.  One workgroup = one KV group g and one or two row tiles.
-// ---------------------------------------------------------------------------
 // Paged cache description ("FlashAttention and inference kernels", section
 // PagedAttention): position t lives at slot t % page_size of physical page
 // table[t / page_size]; kc/vc then point at [num_blocks][page_size][8][64].
@@ -157,6 +160,10 @@ struct KeySplit {
 };
 
 enum Mode { kPlain = 0, kPaged = 1, kSplit = 2 };
+
+// ---------------------------------------------------------------------------
+// The kernel.  One workgroup = one KV group g and one or two row tiles.
+// ---------------------------------------------------------------------------
 
 template <typename T, int NW, int KS, int MODE>
 __global__ void __launch_bounds__(64 * NW * KS)

@@ -228,3 +228,29 @@ def test_binding_rejects_bad_tensors_without_gpu():
         cpf.attn_prefill(q.double(), k.double(), k.double())
     with pytest.raises(ValueError):
         cpf.attn_prefill(q, torch.zeros(4, 8, 64), torch.zeros(4, 8, 64), P=2)
+
+
+def test_every_binding_rejects_host_tensors_and_bad_shapes():
+    """Each wrapper checks dtypes, shapes and placement before it calls the
+    library (none of these reach a kernel)."""
+    import torch
+    q = torch.zeros(3, 32, 64)
+    k = torch.zeros(5, 8, 64)
+    table = torch.zeros(1, dtype=torch.int32)
+    pages = torch.zeros(2, 16, 8, 64)
+    with pytest.raises(ValueError):
+        cpf.attn_prefill_paged(q, pages, pages, table, 2)
+    with pytest.raises(TypeError):
+        cpf.attn_prefill_paged(q, pages.double(), pages.double(), table, 2)
+    with pytest.raises(ValueError):
+        cpf.attn_prefill_paged(q, pages, pages, table.long(), 2)
+    with pytest.raises(ValueError):
+        cpf.attn_prefill_splitkv(q, k, k)
+    with pytest.raises(ValueError):
+        cpf.attn_prefill_rowwise(q, k, k)
+    with pytest.raises(TypeError):
+        cpf.attn_naive(q.bfloat16(), k.bfloat16(), k.bfloat16())
+    with pytest.raises(ValueError):
+        cpf.attn_naive(q, torch.zeros(3, 8, 64), torch.zeros(3, 8, 64))
+    with pytest.raises(ValueError):
+        cpf.attn_naive(q, torch.zeros(4, 8, 64), torch.zeros(4, 8, 64))
