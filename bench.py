@@ -252,6 +252,20 @@ def main():
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
+    # per-launch spread: 20 calls, each between its own pair of events
+    pairs = []
+    for _ in range(20):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    each = sorted(a.elapsed_time(b) for a, b in pairs)
+    launch_ms = {"median": round(each[len(each) // 2], 5), "min": round(each[0], 5), "max": round(each[-1], 5),
+                 "n": len(each)}
+
     flop = cpf.flops(C, P)
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (kernel_ms * 1e-3) / 1e12
@@ -280,6 +294,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic_entry(name),
                      "kernel": KERNEL_NAME, "kernel_ms": round(kernel_ms, 5)},
+        "launch_ms": launch_ms,
         "parity": {"sampled_rows_ok": ok, "max_abs_err": maxerr},
     }
     esz = 4 if dt == "f32" else 2
