@@ -850,7 +850,8 @@ attn_decode_split_kernel(const float* __restrict__ q, const float* __restrict__ 
         }
     }
     __syncthreads();
-    const int h = tid >> 6, d = tid & 63;   // 256 threads = 4 heads x 64 dims
+    if (tid >= 4 * kD) return;              // the first 256 threads: 4 heads x 64 dims
+    const int h = tid >> 6, d = tid & 63;
     float mm = sm[0][h][kD];
 #pragma unroll
     for (int v = 1; v < kDecWaves; ++v) mm = fmaxf(mm, sm[v][h][kD]);
