@@ -43,8 +43,11 @@
 //   does the same causal work.
 // * exp is evaluated as exp2 with log2(e)/8 folded in (into Q for fp32, into an
 //   FMA for bf16).  The running maximum is only moved when a sub-block's
-//   maximum exceeds it by more than 8 in log2 units; any reference value gives
-//   the same softmax because it cancels in O/l, and p stays <= 2^8.
+//   maximum exceeds it by more than 8 in log2 units (a threshold kept in the
+//   scores' own units, so the check is one compare); any reference value gives
+//   the same softmax because it cancels in O/l, and p stays <= 2^8.  It starts
+//   at -1e30, finite and below any score, so a masked (-inf) score gives a
+//   zero weight with no special case.
 //
 // Other kernels in this file: the same kernel in paged-cache and key-split
 // modes, an FMA kernel for one fp32 decode token, the merge of key-split
@@ -68,6 +71,7 @@ constexpr float kScaleLog2 = 0.18033688011112042f;
 // Move the running maximum only when a tile raises it by more than this many
 // powers of two.
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kInvScaleLog2 = 5.545177444479562f;   // 8 / log2(e)
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
@@ -330,7 +334,8 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         }
 
         f16v o0 = {}, o1 = {};   // O^T for dims 0..31 and 32..63
-        float m = -INFINITY;     // running max (log2 units)
+        float m = -1e30f;        // running max (log2 units); finite, below any score
+        float thr = -1e30f;      // rescale when a block maximum exceeds this
         float l = 0.f;           // this lane's share of the running denominator
 
         // ---- per-lane LDS offsets of the MFMA operands (swizzle folded in) ----
@@ -399,11 +404,14 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
 #pragma unroll
             for (int r = 1; r < 16; ++r) bm = fmaxf(bm, s[r]);
             bm = half_max(bm);
-            if constexpr (!kF32) bm *= kScaleLog2;      // bf16 scores are raw dot products
-            const bool upd = bm > m + kRescaleSlack;
+            const bool upd = bm > thr;                  // thr: m + slack, in the scores' own units
             if (__ballot(upd)) {
-                const float alpha = upd ? fast_exp2(m - bm) : 1.0f;
-                if (upd) m = bm;
+                const float bl = kF32 ? bm : bm * kScaleLog2;   // bf16 scores are raw dot products
+                const float alpha = upd ? fast_exp2(m - bl) : 1.0f;
+                if (upd) {
+                    m = bl;
+                    thr = kF32 ? m + kRescaleSlack : (m + kRescaleSlack) * kInvScaleLog2;
+                }
                 l *= alpha;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -411,7 +419,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     o1[r] *= alpha;
                 }
             }
-            const float mu = m == -INFINITY ? 0.f : m;
+            const float mu = m;
             float p[16];
             if constexpr (kF32) {
                 float ps = 0.f;
@@ -536,8 +544,8 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     const float m2 = src[32 * 64];
                     const float l2 = src[33 * 64];
                     const float mx = fmaxf(m, m2);
-                    const float a = m == -INFINITY ? 0.f : fast_exp2(m - mx);
-                    const float b = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mx);
+                    const float a = fast_exp2(m - mx);
+                    const float b = fast_exp2(m2 - mx);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         o0[r] = a * o0[r] + b * src[r * 64];
