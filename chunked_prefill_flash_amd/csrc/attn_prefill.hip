@@ -57,6 +57,8 @@
 #include <stdint.h>
 #include <limits.h>
 
+#include <type_traits>
+
 #include "attn_prefill.h"
 
 namespace {
@@ -369,9 +371,39 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             }
         }
 
+        // ---- bf16 V operands of a sub-block, read ahead ----
+        // Transposed LDS reads: within each 16-lane group, lane j points at 4 dims
+        // of key K0 + j/4 and receives dim D0 + j of keys K0..K0+3, which is the A
+        // operand V^T[dim][key] of the PV MFMA.  The compiler cannot tell these
+        // reads apart from the LDS writes of loads in flight and would wait for
+        // every outstanding load before them, so each tile's are made before the
+        // next tile's loads are issued.
+        struct VOpsBf16 {
+            bf8 a[2][2];                         // [key half u][dim half nt]
+        };
+        struct NoVOps {};                        // fp32 reads V inside the sub-block
+        using VOps = std::conditional_t<kF32, NoVOps, VOpsBf16>;
+        auto read_v = [&](auto stage_off, auto sbc) {
+            constexpr int kStage = decltype(stage_off)::value;
+            constexpr int sb = decltype(sbc)::value;
+            const unsigned char* Vs = lds_raw + kStage + G::kTileBytes + 32 * sb * kRB;
+            VOpsBf16 vo;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const unsigned char* a = Vs + 16 * u * kRB + voff[nt];
+                    const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
+                    const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 8 * kRB));
+                    vo.a[u][nt] = __builtin_shufflevector(__builtin_bit_cast(bf4, h0), __builtin_bit_cast(bf4, h1),
+                                                          0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            return vo;
+        };
+
         // ---- one 32-key sub-block: scores, mask, online softmax, PV ----
         // `stage_off` and `sb` are compile-time constants at every call.
-        auto sub_block = [&](auto stage_off, auto sbc, int jb) {
+        auto sub_block = [&](auto stage_off, auto sbc, int jb, const VOps& vo) {
             constexpr int kStage = decltype(stage_off)::value;
             constexpr int sb = decltype(sbc)::value;
             const unsigned char* Ks = lds_raw + kStage + 32 * sb * kRB;
@@ -442,9 +474,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     o1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32], p[t4], o1, 0, 0, 0);
                 }
             } else {
-                // Transposed LDS reads: within each 16-lane group, lane j points at
-                // 4 dims of key K0 + j/4 and receives dim D0 + j of keys K0..K0+3,
-                // which is the A operand V^T[dim][key] of the PV MFMA.
+                (void)Vs;
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     bf8 pb;
@@ -455,38 +485,36 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
 #pragma unroll
                     for (int e = 0; e < 8; e += 2)
                         l = __builtin_amdgcn_fdot2_f32_bf16(bf2{pb[e], pb[e + 1]}, kOnes, l, false);
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const unsigned char* a = Vs + 16 * u * kRB + voff[nt];
-                        const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
-                        const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a + 8 * kRB));
-                        const bf8 va = __builtin_shufflevector(__builtin_bit_cast(bf4, h0), __builtin_bit_cast(bf4, h1),
-                                                               0, 1, 2, 3, 4, 5, 6, 7);
-                        if (nt == 0)
-                            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o0, 0, 0, 0);
-                        else
-                            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o1, 0, 0, 0);
+                    if constexpr (!kF32) {
+                        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.a[u][0], pb, o0, 0, 0, 0);
+                        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.a[u][1], pb, o1, 0, 0, 0);
                     }
                 }
             }
         };
 
-        // this wave's sub-blocks of tile t, read from the stage at byte offset kStage
-        auto consume = [&](auto stage_off, int t) {
-            if (!wave_active) return;
-            [&]<int... I>(std::integer_sequence<int, I...>) {
-                (([&] {
-                     constexpr int sb = KS * I;
-                     const int sbw = sb + wp;           // wp is runtime; sb + wp < kNB
-                     const int jb = kb + t * kBK + 32 * sbw;
-                     if (jb > w_last) return;
-                     // dispatch on the runtime split index so every offset is an immediate
-                     [&]<int... W>(std::integer_sequence<int, W...>) {
-                         ((wp == W ? (sub_block(stage_off, std::integral_constant<int, sb + W>{}, jb), 0) : 0), ...);
-                     }(std::make_integer_sequence<int, KS>{});
-                 }()),
-                 ...);
-            }(std::make_integer_sequence<int, kNB / KS>{});
+        // This wave's sub-block of tile t (sub-block wp: one per wave), read from
+        // the stage at byte offset kStage; the dispatch on the runtime split index
+        // keeps every LDS offset an immediate.
+        static_assert(kNB == KS, "each wave takes exactly one 32-key sub-block of a tile");
+        auto active = [&](int t) { return wave_active && kb + t * kBK + 32 * wp <= w_last; };
+        auto prefetch_v = [&](auto stage_off, int t) {
+            VOps vo{};
+            if constexpr (!kF32) {
+                if (active(t)) {
+                    [&]<int... W>(std::integer_sequence<int, W...>) {
+                        ((wp == W ? (vo = read_v(stage_off, std::integral_constant<int, W>{}), 0) : 0), ...);
+                    }(std::make_integer_sequence<int, KS>{});
+                }
+            }
+            return vo;
+        };
+        auto consume = [&](auto stage_off, int t, const VOps& vo) {
+            if (!active(t)) return;
+            const int jb = kb + t * kBK + 32 * wp;
+            [&]<int... W>(std::integer_sequence<int, W...>) {
+                ((wp == W ? (sub_block(stage_off, std::integral_constant<int, W>{}, jb, vo), 0) : 0), ...);
+            }(std::make_integer_sequence<int, KS>{});
         };
 
         // ---- key loop over staged tiles (double-buffered, unrolled by two) ----
@@ -499,22 +527,24 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // (every wave issued those before the previous barrier).
         for (int t = 0; t < ntiles; t += 2) {
             PageRef ph{-1, 0};
+            VOps vo = prefetch_v(std::integral_constant<int, 0>{}, t);
             if (t + 1 < ntiles) issue_tile(t + 1, stage1);
             if constexpr (PAGED) {
                 if (t + 2 < ntiles) ph = fetch_page(t + 2);
             }
-            consume(std::integral_constant<int, 0>{}, t);
+            consume(std::integral_constant<int, 0>{}, t, vo);
             __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile t+1 has landed
             if constexpr (PAGED) {
                 if (t + 2 < ntiles) store_offset(t + 2, ph);
             }
             __syncthreads();
             if (t + 1 < ntiles) {
+                vo = prefetch_v(std::integral_constant<int, G::kStageBytes>{}, t + 1);
                 if (t + 2 < ntiles) issue_tile(t + 2, stage0);
                 if constexpr (PAGED) {
                     if (t + 3 < ntiles) ph = fetch_page(t + 3);
                 }
-                consume(std::integral_constant<int, G::kStageBytes>{}, t + 1);
+                consume(std::integral_constant<int, G::kStageBytes>{}, t + 1, vo);
                 __builtin_amdgcn_s_waitcnt(0x3f70);
                 if constexpr (PAGED) {
                     if (t + 3 < ntiles) store_offset(t + 3, ph);
