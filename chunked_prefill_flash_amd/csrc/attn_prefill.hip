@@ -139,7 +139,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // other, so both lanes combine the same two values and agree bitwise.
 __device__ __forceinline__ float half_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -432,9 +432,11 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     if (key > lim) s[r] = -INFINITY;
                 }
             }
+            // NaN-propagating maximum (v_maximum3_f32): unlike fmaxf it needs no
+            // quieting of the MFMA results first, and scores are never NaN
             float bm = s[0];
 #pragma unroll
-            for (int r = 1; r < 16; ++r) bm = fmaxf(bm, s[r]);
+            for (int r = 1; r < 16; ++r) bm = __builtin_elementwise_maximum(bm, s[r]);
             bm = half_max(bm);
             const bool upd = bm > thr;                  // thr: m + slack, in the scores' own units
             if (__ballot(upd)) {
