@@ -12,6 +12,18 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
+def pytest_sessionstart(session):
+    # A fresh checkout has no built library: compile it (hipcc cross-compiles
+    # for gfx950 without a GPU) so the host-side ABI tests can load it.  GPU
+    # runs use the library built beforehand and never reach this.
+    from chunked_prefill_flash_amd import build as hip_build
+    if not os.path.exists(hip_build.LIB):
+        try:
+            hip_build.build()
+        except Exception as exc:  # the ABI tests then report the missing library
+            sys.stderr.write("could not build the HIP library: %s\n" % exc)
+
+
 def pytest_collection_modifyitems(config, items):
     # GPU tests are collected everywhere but skipped when no GPU is visible, so a
     # plain `pytest` on a CPU-only machine stays green.  On a GPU machine they run.
