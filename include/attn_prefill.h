@@ -31,6 +31,10 @@
  * waiting; the caller synchronises.  `out` must not overlap the inputs; every
  * element of out[0..C) is overwritten.
  *
+ * Every entry point only enqueues kernels on `stream`: it allocates,
+ * synchronises and memsets nothing, so calls can be captured in a HIP graph
+ * and replayed (with the same pointers and sizes).
+ *
  * Errors: nothing is thrown across the ABI; each call returns an
  * attn_status_t and enqueues no work unless it returns ATTN_OK.
  */
