@@ -43,11 +43,14 @@
 //   does the same causal work.
 // * exp is evaluated as exp2 with log2(e)/8 folded in (into Q for fp32, into an
 //   FMA for bf16).  The running maximum is only moved when a sub-block's
-//   maximum exceeds it by more than 8 in log2 units (a threshold kept in the
-//   scores' own units, so the check is one compare); any reference value gives
-//   the same softmax because it cancels in O/l, and p stays <= 2^8.  It starts
-//   at -1e30, finite and below any score, so a masked (-inf) score gives a
-//   zero weight with no special case.
+//   maximum exceeds it by more than 8 in log2 units; any reference value
+//   gives the same softmax because it cancels in O/l, and p stays <= 2^8.
+//   The weights are formed against the current maximum first: a lane's sum
+//   bounds each of its weights, so one compare of that sum with 2^8 replaces
+//   the block maximum, which is only formed (and the weights redone) in a wave
+//   where some sum passes it.  The maximum starts at -1e30, finite and below
+//   any score, so a masked (-inf) score gives a zero weight with no special
+//   case.
 //
 // Other kernels in this file: the same kernel in paged-cache and key-split
 // modes, an FMA kernel for one fp32 decode token, the merge of key-split
@@ -73,8 +76,10 @@ constexpr float kScaleLog2 = 0.18033688011112042f;
 // Move the running maximum only when a tile raises it by more than this many
 // powers of two.
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kSlackWeight = 256.0f;                // 2^kRescaleSlack
 constexpr float kInvScaleLog2 = 5.545177444479562f;   // 8 / log2(e)
 
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
@@ -97,7 +102,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 // Tile geometry for a workgroup of NW row-waves x KS key-split waves.
 //
 // LDS holds each staged K and V tile as unpadded key-major rows (256 B fp32,
-// 128 B bf16), in two stages.  Inside a row the 16-byte chunks are permuted
+// 128 B bf16), in two stages, laid out V0 V1 K0 K1: every V operand then sits
+// below 64 KiB and every K operand below 64 KiB of a per-lane base, so each
+// LDS read is one base register plus an immediate offset (the DS offset field
+// is 16 bits).  Inside a row the 16-byte chunks are permuted
 // by XOR with a per-row code so that the MFMA operand reads (32 lanes on 32
 // different keys, same chunk) and the bf16 transposed V reads (16 lanes on a
 // 4-key x 16-dim block) spread over all LDS banks; unpadded rows let each
@@ -111,7 +119,10 @@ struct Geo {
     static constexpr int kRows = 8 * NW;             // chunk rows per work item
     static constexpr int kRowBytes = kD * Elem<T>::kBytes;
     static constexpr int kTileBytes = kBK * kRowBytes;                // one tensor, one stage
-    static constexpr int kStageBytes = 2 * kTileBytes;                // K then V
+    static constexpr int kStageBytes = 2 * kTileBytes;                // K and V of one stage
+    static constexpr int kKBase = 2 * kTileBytes;                     // K0 follows V0 and V1
+    static constexpr int kKSpan = 4 * kTileBytes - kKBase;            // K0 and K1
+    static_assert(2 * kTileBytes <= 65536 && kKSpan <= 65536, "LDS operand offsets must fit 16 bits");
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;             // rows per 64-lane 16 B load
     static constexpr int kLoadsPerTile = 2 * kBK / kRowsPerLoad;      // K and V
     static constexpr int kLoadsPerWave = (kLoadsPerTile + kWaves - 1) / kWaves;
@@ -183,8 +194,6 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     constexpr bool SPLIT = MODE == kSplit;
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[G::kLdsBytes];
-    unsigned char* const stage0 = lds_raw;
-    unsigned char* const stage1 = lds_raw + G::kStageBytes;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -256,7 +265,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     ? (uint32_t)(((size_t)r.ph * pg.page_size + r.slot) * kHKV + g) * kRB
                     : kNoRow;
     };
-    auto issue_tile = [&](int t, unsigned char* stage) {
+    auto issue_tile = [&](int t, int stage) {
         const int key0 = kb + t * kBK;
         uint32_t range;
         size_t base;
@@ -283,7 +292,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             } else {
                 voff = (uint32_t)(row * kHKV + g) * kRB + lc * 16;
             }
-            unsigned char* dst = stage + tensor * G::kTileBytes + (row - rl) * kRB;
+            unsigned char* dst = lds_raw + (tensor ? 0 : G::kKBase) + stage * G::kTileBytes + (row - rl) * kRB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(tensor ? rv : rk, (lds_void_t*)dst, 16, voff, 0, 0, 0);
         }
     };
@@ -311,7 +320,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             if (ntiles > 1) store_offset(1, ph1);
             __syncthreads();
         }
-        issue_tile(0, stage0);
+        issue_tile(0, 0);
 
         // ---- Q operand (B of S^T = K Q^T), held for the whole key loop ----
         // fp32: qf[s] = q[row][head][32*hh + s] * log2(e)/8, s = 0..31
@@ -335,7 +344,10 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             }
         }
 
-        f16v o0 = {}, o1 = {};   // O^T for dims 0..31 and 32..63
+        // O^T accumulators.  bf16: o0 holds dims 0..31 and o1 dims 32..63; fp32:
+        // o0 holds the even dims and o1 the odd ones (row m of each is dim 2m or
+        // 2m+1), so one 8-byte LDS read gives a lane both of its V operands.
+        f16v o0 = {}, o1 = {};
         float m = -1e30f;        // running max (log2 units); finite, below any score
         float thr = -1e30f;      // rescale when a block maximum exceeds this
         float l = 0.f;           // this lane's share of the running denominator
@@ -345,22 +357,22 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // stage, tile and sub-block offset is a multiple of 8 rows, so each lane's
         // operand addresses are a handful of fixed offsets plus immediates.
         //  fp32 K: chunk 8*hh + c of row n           (c = 0..7)
-        //  fp32 V: dwords n and n+32 of row 4*hh + q   (q = 0..3; row + 8*(t/4))
+        //  fp32 V: dwords 2n, 2n+1 of row 4*hh + q   (q = 0..3; row + 8*(t/4))
         //  bf16 K: chunk 2*st + hh of row n          (st = 0..3)
         //  bf16 V: transposed 4-key x 16-dim blocks, one offset per 32-dim half
         int koff[kF32 ? 8 : 4];
         int voff[kF32 ? 4 : 2];
         if constexpr (kF32) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) koff[c] = n * kRB + (((8 * hh + c) ^ chunk_code<T>(n)) * 16);
+            for (int c = 0; c < 8; ++c) koff[c] = G::kKBase + n * kRB + (((8 * hh + c) ^ chunk_code<T>(n)) * 16);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int r = 4 * hh + q4;
-                voff[q4] = r * kRB + (((n >> 2) ^ chunk_code<T>(r)) * 16) + (n & 3) * 4;
+                voff[q4] = r * kRB + (((n >> 1) ^ chunk_code<T>(r)) * 16) + (n & 1) * 8;
             }
         } else {
 #pragma unroll
-            for (int st = 0; st < 4; ++st) koff[st] = n * kRB + (((2 * st + hh) ^ chunk_code<T>(n)) * 16);
+            for (int st = 0; st < 4; ++st) koff[st] = G::kKBase + n * kRB + (((2 * st + hh) ^ chunk_code<T>(n)) * 16);
             const int grp = (lane >> 4) & 1;
             const int j = lane & 15;
             const int r = 4 * hh + (j >> 2);            // row within an 8-row block
@@ -383,10 +395,10 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         };
         struct NoVOps {};                        // fp32 reads V inside the sub-block
         using VOps = std::conditional_t<kF32, NoVOps, VOpsBf16>;
-        auto read_v = [&](auto stage_off, auto sbc) {
-            constexpr int kStage = decltype(stage_off)::value;
+        auto read_v = [&](auto stage_c, auto sbc) {
+            constexpr int kStage = decltype(stage_c)::value;
             constexpr int sb = decltype(sbc)::value;
-            const unsigned char* Vs = lds_raw + kStage + G::kTileBytes + 32 * sb * kRB;
+            const unsigned char* Vs = lds_raw + kStage * G::kTileBytes + 32 * sb * kRB;
             VOpsBf16 vo;
 #pragma unroll
             for (int u = 0; u < 2; ++u)
@@ -402,12 +414,13 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         };
 
         // ---- one 32-key sub-block: scores, mask, online softmax, PV ----
-        // `stage_off` and `sb` are compile-time constants at every call.
-        auto sub_block = [&](auto stage_off, auto sbc, int jb, const VOps& vo) {
-            constexpr int kStage = decltype(stage_off)::value;
+        // `stage_c` and `sb` are compile-time constants at every call; the K
+        // offsets koff[] carry the K region's base.
+        auto sub_block = [&](auto stage_c, auto sbc, int jb, const VOps& vo) {
+            constexpr int kStage = decltype(stage_c)::value;
             constexpr int sb = decltype(sbc)::value;
-            const unsigned char* Ks = lds_raw + kStage + 32 * sb * kRB;
-            const unsigned char* Vs = lds_raw + kStage + G::kTileBytes + 32 * sb * kRB;
+            const unsigned char* Ks = lds_raw + kStage * G::kTileBytes + 32 * sb * kRB;
+            const unsigned char* Vs = lds_raw + kStage * G::kTileBytes + 32 * sb * kRB;
             f16v s = {};
             if constexpr (kF32) {
 #pragma unroll
@@ -432,15 +445,17 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     if (key > lim) s[r] = -INFINITY;
                 }
             }
-            // NaN-propagating maximum (v_maximum3_f32): unlike fmaxf it needs no
-            // quieting of the MFMA results first, and scores are never NaN
-            float bm = s[0];
+            // Lazy rescale: m moves only when a block maximum exceeds it by more
+            // than kRescaleSlack (log2 units), so every weight stays within
+            // 2^slack.  The block maximum uses the NaN-propagating v_maximum3_f32,
+            // which unlike fmaxf needs no quieting of the MFMA results first.
+            auto block_max = [&]() {
+                float bm = s[0];
 #pragma unroll
-            for (int r = 1; r < 16; ++r) bm = __builtin_elementwise_maximum(bm, s[r]);
-            bm = half_max(bm);
-            const bool upd = bm > thr;                  // thr: m + slack, in the scores' own units
-            if (__ballot(upd)) {
-                const float bl = kF32 ? bm : bm * kScaleLog2;   // bf16 scores are raw dot products
+                for (int r = 1; r < 16; ++r) bm = __builtin_elementwise_maximum(bm, s[r]);
+                return half_max(bm);
+            };
+            auto rescale = [&](float bl, bool upd) {   // bl: block maximum, log2 units
                 const float alpha = upd ? fast_exp2(m - bl) : 1.0f;
                 if (upd) {
                     m = bl;
@@ -452,51 +467,78 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     o0[r] *= alpha;
                     o1[r] *= alpha;
                 }
-            }
-            const float mu = m;
+            };
             float p[16];
             if constexpr (kF32) {
-                float ps = 0.f;
+                // Weights first, against the current m.  Their lane sum bounds each
+                // of them, so the block maximum is formed only in a wave where some
+                // lane's sum exceeds 2^slack; there the rescale test is the usual
+                // one (a lane whose maximum passes it always has such a sum).
+                auto weights = [&]() {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    p[r] = fast_exp2(s[r] - mu);
-                    ps += p[r];
+                    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(s[r] - m);
+                    float ps = p[0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) ps += p[r];
+                    return ps;
+                };
+                float ps = weights();
+                if (__ballot(ps > kSlackWeight)) {
+                    const float bm = block_max();
+                    rescale(bm, bm > thr);
+                    ps = weights();
                 }
                 l += ps;
-            } else {
+            }
+            bf8 pbv[2];   // bf16: the weights rounded to nearest even, PV operand B
+            if constexpr (!kF32) {
+                // Same scheme on the rounded weights (bf16 scores are raw dot
+                // products: thr is in raw units); the denominator sums exactly
+                // the weights the PV product uses.
+                constexpr bf2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+                auto weights = [&]() {
+                    const float mu = m;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], kScaleLog2, -mu));
+                    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], kScaleLog2, -mu));
+                    float ps = 0.f;
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) pbv[u][e] = (__bf16)p[8 * u + e];
+#pragma unroll
+                        for (int e = 0; e < 8; e += 2)
+                            ps = __builtin_amdgcn_fdot2_f32_bf16(bf2{pbv[u][e], pbv[u][e + 1]}, kOnes, ps, false);
+                    }
+                    return ps;
+                };
+                float ps = weights();
+                if (__ballot(ps > kSlackWeight)) {
+                    const float bm = block_max();
+                    rescale(bm * kScaleLog2, bm > thr);
+                    ps = weights();
+                }
+                l += ps;
             }
             if constexpr (kF32) {
-                // key 8(t/4) + 4hh + t%4 of the sub-block: V[key][n] and V[key][n+32]
+                // key 8(t/4) + 4hh + t%4 of the sub-block: V[key][2n] and V[key][2n+1]
 #pragma unroll
                 for (int t4 = 0; t4 < 16; ++t4) {
-                    const float* vr = reinterpret_cast<const float*>(Vs + 8 * (t4 >> 2) * kRB + voff[t4 & 3]);
+                    const f2 vr = *reinterpret_cast<const f2*>(Vs + 8 * (t4 >> 2) * kRB + voff[t4 & 3]);
                     o0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[0], p[t4], o0, 0, 0, 0);
-                    o1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32], p[t4], o1, 0, 0, 0);
+                    o1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[1], p[t4], o1, 0, 0, 0);
                 }
             } else {
                 (void)Vs;
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    bf8 pb;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[8 * u + e];
-                    // the denominator sums the same rounded weights the PV product uses
-                    constexpr bf2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2)
-                        l = __builtin_amdgcn_fdot2_f32_bf16(bf2{pb[e], pb[e + 1]}, kOnes, l, false);
-                    if constexpr (!kF32) {
-                        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.a[u][0], pb, o0, 0, 0, 0);
-                        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.a[u][1], pb, o1, 0, 0, 0);
-                    }
+                    o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.a[u][0], pbv[u], o0, 0, 0, 0);
+                    o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo.a[u][1], pbv[u], o1, 0, 0, 0);
                 }
             }
         };
 
         // This wave's sub-block of tile t (sub-block wp: one per wave), read from
-        // the stage at byte offset kStage; the dispatch on the runtime split index
+        // stage kStage; the dispatch on the runtime split index
         // keeps every LDS offset an immediate.
         static_assert(kNB == KS, "each wave takes exactly one 32-key sub-block of a tile");
         auto active = [&](int t) { return wave_active && kb + t * kBK + 32 * wp <= w_last; };
@@ -530,7 +572,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         for (int t = 0; t < ntiles; t += 2) {
             PageRef ph{-1, 0};
             VOps vo = prefetch_v(std::integral_constant<int, 0>{}, t);
-            if (t + 1 < ntiles) issue_tile(t + 1, stage1);
+            if (t + 1 < ntiles) issue_tile(t + 1, 1);
             if constexpr (PAGED) {
                 if (t + 2 < ntiles) ph = fetch_page(t + 2);
             }
@@ -541,12 +583,12 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             }
             __syncthreads();
             if (t + 1 < ntiles) {
-                vo = prefetch_v(std::integral_constant<int, G::kStageBytes>{}, t + 1);
-                if (t + 2 < ntiles) issue_tile(t + 2, stage0);
+                vo = prefetch_v(std::integral_constant<int, 1>{}, t + 1);
+                if (t + 2 < ntiles) issue_tile(t + 2, 0);
                 if constexpr (PAGED) {
                     if (t + 3 < ntiles) ph = fetch_page(t + 3);
                 }
-                consume(std::integral_constant<int, G::kStageBytes>{}, t + 1, vo);
+                consume(std::integral_constant<int, 1>{}, t + 1, vo);
                 __builtin_amdgcn_s_waitcnt(0x3f70);
                 if constexpr (PAGED) {
                     if (t + 3 < ntiles) store_offset(t + 3, ph);
@@ -590,17 +632,36 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         }
 
         // ---- epilogue: one division per query, fp32 stores ----
+        // This lane's 32 values of its (row, head) output vector, times sc, in
+        // dim order; accumulator element r sits in row 8(r/4) + 4hh + r%4 of
+        // its 32-row block.
+        auto store_o = [&](float* vec, float sc) {
+            if constexpr (kF32) {
+                float* dst = vec + 8 * hh;   // rows 8a+4hh+j: dims 16a+8hh+2j (o0), +1 (o1)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    *reinterpret_cast<f4*>(dst + 16 * a) =
+                        f4{o0[4 * a] * sc, o1[4 * a] * sc, o0[4 * a + 1] * sc, o1[4 * a + 1] * sc};
+                    *reinterpret_cast<f4*>(dst + 16 * a + 4) =
+                        f4{o0[4 * a + 2] * sc, o1[4 * a + 2] * sc, o0[4 * a + 3] * sc, o1[4 * a + 3] * sc};
+                }
+            } else {
+                float* dst = vec + 4 * hh;   // rows 8a+4hh+j: dims 8a+4hh+j (o0), +32 (o1)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    *reinterpret_cast<f4*>(dst + 8 * a) =
+                        f4{o0[4 * a] * sc, o0[4 * a + 1] * sc, o0[4 * a + 2] * sc, o0[4 * a + 3] * sc};
+                    *reinterpret_cast<f4*>(dst + 32 + 8 * a) =
+                        f4{o1[4 * a] * sc, o1[4 * a + 1] * sc, o1[4 * a + 2] * sc, o1[4 * a + 3] * sc};
+                }
+            }
+        };
         if constexpr (SPLIT) {
             // key split: unnormalised partial O, running max m and denominator l
             if (wp == 0 && wave_active && row < C) {
                 const float lt = half_sum(l);
                 const size_t qi = ((size_t)split * C + row) * kHQ + head;
-                float* dst = ks.part + qi * kD + 4 * hh;
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    *reinterpret_cast<f4*>(dst + 8 * a) = f4{o0[4 * a], o0[4 * a + 1], o0[4 * a + 2], o0[4 * a + 3]};
-                    *reinterpret_cast<f4*>(dst + 32 + 8 * a) = f4{o1[4 * a], o1[4 * a + 1], o1[4 * a + 2], o1[4 * a + 3]};
-                }
+                store_o(ks.part + qi * kD, 1.0f);
                 if (hh == 0) {
                     float* ml = ks.part + (size_t)ks.n * C * kHQ * kD + qi * 2;
                     ml[0] = m;
@@ -611,16 +672,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             (void)ks;
             const float lt = half_sum(l);
             const float inv = 1.0f / lt;
-            if (row < C) {
-                float* dst = out + ((size_t)row * kHQ + head) * kD + 4 * hh;
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    *reinterpret_cast<f4*>(dst + 8 * a) =
-                        f4{o0[4 * a] * inv, o0[4 * a + 1] * inv, o0[4 * a + 2] * inv, o0[4 * a + 3] * inv};
-                    *reinterpret_cast<f4*>(dst + 32 + 8 * a) =
-                        f4{o1[4 * a] * inv, o1[4 * a + 1] * inv, o1[4 * a + 2] * inv, o1[4 * a + 3] * inv};
-                }
-            }
+            if (row < C) store_o(out + ((size_t)row * kHQ + head) * kD, inv);
         }
         __syncthreads();   // LDS is reused by the next work item
     }
@@ -1099,8 +1151,8 @@ hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, 
             if constexpr (MODE == kSplit) return hipErrorInvalidValue;   // never planned
             else return launch<T, 4, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
         case kV_2x4: return launch<T, 2, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
-        case kV_4x4:
-            if constexpr (MODE == kSplit || (MODE == kPaged && sizeof(T) == 4)) return hipErrorInvalidValue;
+        case kV_4x4:   // planned for fp32 contiguous caches only
+            if constexpr (MODE != kPlain || sizeof(T) != 4) return hipErrorInvalidValue;
             else return launch<T, 4, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
         default: return launch<T, 1, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
     }
