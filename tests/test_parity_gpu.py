@@ -186,6 +186,34 @@ def test_every_row_max_in_its_last_tile():
     full_check("monotone", 150, 200, "f32")
 
 
+@pytest.mark.parametrize("C", [40, 300, 1100])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lazy_rescale_false_alarm_then_jump(C, dtype):
+    """Head-independent scores (q = 8 e_0, so a key's score is K[j][g][0]) of
+    0 on keys 0..127, 6 log2-units on keys 128..255, 10 on keys 256..383 and 0
+    after.  Every wave of every launch shape meets the 0 block first (staged
+    tiles are 64 or 128 keys, key splits take 32-key sub-blocks in order), so
+    in the second block each lane's 16 weights are 2^6: their sum passes 2^8
+    while the block maximum stays 2 under the rescale threshold (a false alarm:
+    weights recomputed, no rescale); the third block moves the maximum by 10
+    (a real rescale), and the last rows' weights are 2^-10."""
+    P = 512
+    T = P + C
+    rng = np.random.default_rng(7700 + C)
+    q = np.zeros((C, HQ, D), np.float32)
+    q[:, :, 0] = 8.0
+    k = rng.standard_normal((T, HKV, D)).astype(np.float32)
+    k[:, :, 0] = 0.0
+    k[128:256, :, 0] = 6.0 * np.log(2.0)
+    k[256:384, :, 0] = 10.0 * np.log(2.0)
+    v = rng.standard_normal((T, HKV, D)).astype(np.float32)
+    qo, ko, vo = oracle_inputs(q, dtype), oracle_inputs(k, dtype), oracle_inputs(v, dtype)
+    ref = oracle.attn_prefill(qo, ko, vo, P)
+    absref = oracle.attn_prefill(qo, ko, np.abs(vo), P) if dtype == "bf16" else None
+    got = run_gpu(q, k, v, P, dtype)
+    check_close(got, ref, dtype, "step scores C=%d P=%d %s" % (C, P, dtype), absref)
+
+
 def test_zero_length_chunk_is_a_noop():
     q = torch.empty(0, HQ, D, device=dev())
     k = torch.randn(5, HKV, D, device=dev())
