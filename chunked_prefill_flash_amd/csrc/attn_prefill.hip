@@ -86,6 +86,7 @@ typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -248,13 +249,19 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         int ph;     // table entry (-1 past the cache)
         int slot;   // position within the page
     };
+    // The table is read through a buffer descriptor (scalar base, 32-bit lane
+    // offset), and row offsets are formed in 32 bits: the host rejects pools
+    // and tables whose byte sizes do not fit them.
+    const __amdgpu_buffer_rsrc_t rtab = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)pg.table, (short)0, PAGED ? (uint32_t)((total + pg.page_size - 1) / pg.page_size) * 4u : 0u,
+        0x00020000);
     auto fetch_page = [&](int t) {                  // key kb + t*kBK + tid; divides before the tile's math
         const int key = kb + t * kBK + tid;
         PageRef r{-1, 0};
         if (tid < kBK && key < total) {
             const int blk = key / pg.page_size;
             r.slot = key - blk * pg.page_size;
-            r.ph = pg.table[blk];
+            r.ph = (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, (uint32_t)blk * 4u, 0, 0);
         }
         return r;
     };
@@ -262,7 +269,8 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         if (tid < kBK)
             pofs[(t & 1) * kBK + tid] =
                 r.ph >= 0 && r.ph < pg.num_blocks
-                    ? (uint32_t)(((size_t)r.ph * pg.page_size + r.slot) * kHKV + g) * kRB
+                    ? ((uint32_t)r.ph * (uint32_t)pg.page_size + (uint32_t)r.slot) * (uint32_t)(kHKV * kRB) +
+                          (uint32_t)(g * kRB)
                     : kNoRow;
     };
     auto issue_tile = [&](int t, int stage) {
@@ -303,6 +311,12 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         const int i0w = i0 + 8 * wr;
         const int rows_end = min(i0 + kRows, C);
         if constexpr (SPLIT) kb = split * ks.len;
+        if constexpr (PAGED) {
+            // An opaque copy per work item: the page lookups of its first tiles
+            // are then recomputed here instead of being hoisted out of the item
+            // loop and kept live (spilled) across the whole kernel.
+            asm volatile("" : "+s"(kb));
+        }
         const int kv_end = SPLIT ? min(P + rows_end, kb + ks.len) : P + rows_end;
         const int ntiles = kv_end > kb ? (kv_end - kb + kBK - 1) / kBK : 0;
         if (ntiles == 0) continue;                  // this split lies past every row of the item
@@ -325,22 +339,30 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // ---- Q operand (B of S^T = K Q^T), held for the whole key loop ----
         // fp32: qf[s] = q[row][head][32*hh + s] * log2(e)/8, s = 0..31
         // bf16: qb[s] = q[row][head][16*s + 8*hh .. +7], s = 0..3
+        // Loaded through a buffer descriptor over this work item's rows (a
+        // scalar base and a 32-bit lane offset instead of a 64-bit address per
+        // lane); rows past the chunk read as zero.  The output is stored the
+        // same way.
+        const int item_rows = min(kRows, C - i0);
+        const uint32_t lane_vec = (uint32_t)(((row - i0) * kHQ + head) * kD);   // element offset in the item
         float qf[kF32 ? 32 : 1];
         bf8 qb[kF32 ? 1 : 4];
-        if constexpr (kF32) {
-            const float* src = reinterpret_cast<const float*>(q) + ((size_t)row * kHQ + head) * kD + 32 * hh;
+        {
+            const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(q + (size_t)i0 * kHQ * kD), (short)0, (uint32_t)item_rows * kHQ * kD * sizeof(T), 0x00020000);
+            if constexpr (kF32) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                f4 x = row < C ? *reinterpret_cast<const f4*>(src + 4 * c) : f4{0.f, 0.f, 0.f, 0.f};
+                for (int c = 0; c < 8; ++c) {
+                    const f4 x = __builtin_bit_cast(
+                        f4, __builtin_amdgcn_raw_buffer_load_b128(rq, (lane_vec + 32 * hh + 4 * c) * 4, 0, 0));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) qf[4 * c + e] = x[e] * kScaleLog2;
-            }
-        } else {
-            const uint16_t* src = reinterpret_cast<const uint16_t*>(q) + ((size_t)row * kHQ + head) * kD + 8 * hh;
+                    for (int e = 0; e < 4; ++e) qf[4 * c + e] = x[e] * kScaleLog2;
+                }
+            } else {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                u16x8 x = row < C ? *reinterpret_cast<const u16x8*>(src + 16 * s) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-                qb[s] = __builtin_bit_cast(bf8, x);
+                for (int st = 0; st < 4; ++st)
+                    qb[st] = __builtin_bit_cast(
+                        bf8, __builtin_amdgcn_raw_buffer_load_b128(rq, (lane_vec + 8 * hh + 16 * st) * 2, 0, 0));
             }
         }
 
@@ -635,24 +657,29 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // This lane's 32 values of its (row, head) output vector, times sc, in
         // dim order; accumulator element r sits in row 8(r/4) + 4hh + r%4 of
         // its 32-row block.
-        auto store_o = [&](float* vec, float sc) {
+        // `item` points at the output of row i0, head 0; rows past the chunk
+        // fall outside the descriptor and are not written.
+        auto store_o = [&](float* item, float sc) {
+            const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)item, (short)0, (uint32_t)item_rows * kHQ * kD * 4, 0x00020000);
+            auto st4 = [&](uint32_t elem, f4 x) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro, (lane_vec + elem) * 4, 0, 0);
+            };
             if constexpr (kF32) {
-                float* dst = vec + 8 * hh;   // rows 8a+4hh+j: dims 16a+8hh+2j (o0), +1 (o1)
+                // rows 8a+4hh+j: dims 16a+8hh+2j (o0), +1 (o1)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    *reinterpret_cast<f4*>(dst + 16 * a) =
-                        f4{o0[4 * a] * sc, o1[4 * a] * sc, o0[4 * a + 1] * sc, o1[4 * a + 1] * sc};
-                    *reinterpret_cast<f4*>(dst + 16 * a + 4) =
-                        f4{o0[4 * a + 2] * sc, o1[4 * a + 2] * sc, o0[4 * a + 3] * sc, o1[4 * a + 3] * sc};
+                    st4(8 * hh + 16 * a, f4{o0[4 * a] * sc, o1[4 * a] * sc, o0[4 * a + 1] * sc, o1[4 * a + 1] * sc});
+                    st4(8 * hh + 16 * a + 4,
+                        f4{o0[4 * a + 2] * sc, o1[4 * a + 2] * sc, o0[4 * a + 3] * sc, o1[4 * a + 3] * sc});
                 }
             } else {
-                float* dst = vec + 4 * hh;   // rows 8a+4hh+j: dims 8a+4hh+j (o0), +32 (o1)
+                // rows 8a+4hh+j: dims 8a+4hh+j (o0), +32 (o1)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    *reinterpret_cast<f4*>(dst + 8 * a) =
-                        f4{o0[4 * a] * sc, o0[4 * a + 1] * sc, o0[4 * a + 2] * sc, o0[4 * a + 3] * sc};
-                    *reinterpret_cast<f4*>(dst + 32 + 8 * a) =
-                        f4{o1[4 * a] * sc, o1[4 * a + 1] * sc, o1[4 * a + 2] * sc, o1[4 * a + 3] * sc};
+                    st4(4 * hh + 8 * a, f4{o0[4 * a] * sc, o0[4 * a + 1] * sc, o0[4 * a + 2] * sc, o0[4 * a + 3] * sc});
+                    st4(4 * hh + 32 + 8 * a,
+                        f4{o1[4 * a] * sc, o1[4 * a + 1] * sc, o1[4 * a + 2] * sc, o1[4 * a + 3] * sc});
                 }
             }
         };
@@ -661,7 +688,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             if (wp == 0 && wave_active && row < C) {
                 const float lt = half_sum(l);
                 const size_t qi = ((size_t)split * C + row) * kHQ + head;
-                store_o(ks.part + qi * kD, 1.0f);
+                store_o(ks.part + ((size_t)split * C + i0) * kHQ * kD, 1.0f);
                 if (hh == 0) {
                     float* ml = ks.part + (size_t)ks.n * C * kHQ * kD + qi * 2;
                     ml[0] = m;
@@ -672,7 +699,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             (void)ks;
             const float lt = half_sum(l);
             const float inv = 1.0f / lt;
-            if (row < C) store_o(out + ((size_t)row * kHQ + head) * kD, inv);
+            if (row < C) store_o(out + (size_t)i0 * kHQ * kD, inv);
         }
         __syncthreads();   // LDS is reused by the next work item
     }
@@ -1118,9 +1145,9 @@ Plan make_plan(int C, int variant) {
 // 4 key splits.  Short chunks: 8 rows, 4 key splits.
 template <typename T>
 Plan choose_plan(int C, bool paged) {
-    // (the paged fp32 16-wave kernel spills at 128 VGPRs and gains only ~1%; it
-    // uses 8 waves)
-    Plan p = C >= 1024 ? (sizeof(T) == 4 && !paged ? make_plan<T, 4, 4>(C, kV_4x4) : make_plan<T, 4, 2>(C, kV_4x2))
+    // (the paged fp32 16-wave kernel spills a few registers outside its key loop
+    // and is still ~3% faster than the 8-wave one)
+    Plan p = C >= 1024 ? (sizeof(T) == 4 ? make_plan<T, 4, 4>(C, kV_4x4) : make_plan<T, 4, 2>(C, kV_4x2))
              : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4)
                         : make_plan<T, 1, 4>(C, kV_1x4);
     p.lds += 4 * (paged ? 2 * p.bk : 1);   // the page-offset table (one word when unused)
@@ -1151,8 +1178,8 @@ hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, 
             if constexpr (MODE == kSplit) return hipErrorInvalidValue;   // never planned
             else return launch<T, 4, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
         case kV_2x4: return launch<T, 2, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
-        case kV_4x4:   // planned for fp32 contiguous caches only
-            if constexpr (MODE != kPlain || sizeof(T) != 4) return hipErrorInvalidValue;
+        case kV_4x4:   // planned for fp32 only, never with key splits
+            if constexpr (MODE == kSplit || sizeof(T) != 4) return hipErrorInvalidValue;
             else return launch<T, 4, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
         default: return launch<T, 1, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
     }
@@ -1399,6 +1426,7 @@ attn_status_t attn_prefill_paged_validate(const void* q, const void* kPages, con
     if ((mis & 15u) || (reinterpret_cast<uintptr_t>(blockTable) & 3u)) return ATTN_ERR_MISALIGNED;
     const size_t nq = (size_t)C * kHQ * kD, out_bytes = nq * 4;
     const size_t ntab = ((size_t)P + C + pageSize - 1) / pageSize;
+    if (ntab * 4 > 0xFFFFFFFFull) return ATTN_ERR_INVALID_ARG;   // table addressed with 32-bit offsets
     if (overlaps(out, out_bytes, q, nq * esz) || overlaps(out, out_bytes, kPages, pool) ||
         overlaps(out, out_bytes, vPages, pool) || overlaps(out, out_bytes, blockTable, ntab * 4))
         return ATTN_ERR_ALIAS;

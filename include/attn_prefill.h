@@ -118,9 +118,10 @@ attn_status_t attn_prefill_validate(const void* q, const void* kCache, const voi
  *
  * A table entry outside [0, numBlocks) does not fault: the positions it maps
  * read as zeros (the result is then not the attention of any cache).  Returns
- * as attn_prefill; ATTN_ERR_INVALID_ARG also for pageSize <= 0, numBlocks <= 0
- * or a pool too large for 32-bit offsets; ATTN_ERR_ALIAS if out overlaps q, the
- * pools or the table.
+ * as attn_prefill; ATTN_ERR_INVALID_ARG also for pageSize <= 0, numBlocks <= 0,
+ * or a pool or table too large for 32-bit byte offsets (a pool above 4 GiB, or
+ * 2^30 or more table entries); ATTN_ERR_ALIAS if out overlaps q, the pools or
+ * the table.
  */
 attn_status_t attn_prefill_paged(const void* q, const void* kPages, const void* vPages, const int* blockTable,
                                  int numBlocks, int pageSize, float* out, int C, int P, attn_dtype_t dtype,

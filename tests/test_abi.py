@@ -8,6 +8,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import chunked_prefill_flash_amd as cpf
 
@@ -134,6 +135,9 @@ def test_paged_validate_codes():
     assert pv(nb=0) == INVALID
     assert pv(C=-1) == INVALID
     assert pv(nb=1 << 20, ps=16) == INVALID            # pool beyond 32-bit offsets (16M rows x 2 KiB)
+    big_tab = dict(C=1, ps=1, tab=A + 320 * MB)          # table placed after out: no overlap
+    assert pv(P=(1 << 30) - 1, **big_tab) == INVALID     # 2^30 entries: 4 GiB, beyond 32-bit offsets
+    assert pv(P=(1 << 30) - 2, **big_tab) == OK          # 2^30 - 1 entries fit
     assert pv(q=0, kp=0, vp=0, tab=0, out=0, C=0) == OK
     assert pv(tab=0) == NULLP
     assert pv(tab=A + 192 * MB + 2) == MISAL
@@ -143,10 +147,10 @@ def test_paged_validate_codes():
     assert pv(out=A + 64 * MB, kp=A + 64 * MB) == ALIAS
 
 
-def test_paged_plan_avoids_the_16_wave_fp32_kernel():
-    p = cpf.plan(2048, 2048, paged=True)
-    assert p["threads"] == 512
-    assert cpf.plan(2048, 2048)["threads"] == 1024
+def test_long_chunks_use_the_16_wave_fp32_kernel_paged_or_not():
+    for paged in (False, True):
+        assert cpf.plan(2048, 2048, paged=paged)["threads"] == 1024
+        assert cpf.plan(2048, 2048, dtype=torch.bfloat16, paged=paged)["threads"] == 512
 
 
 def test_splitkv_workspace_sizes():

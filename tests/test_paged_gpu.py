@@ -85,12 +85,12 @@ def test_paged_full_size_c2048_p2048():
     check(got, ref, "f32", what="paged C=P=2048")
 
 
-def test_paged_equals_contiguous_bitwise():
+@pytest.mark.parametrize("C,P", [(600, 1000), (1100, 300)])
+def test_paged_equals_contiguous_bitwise(C, P):
     """Same launch plan, same arithmetic: the paged path must reproduce the
-    contiguous path bit for bit."""
-    C, P = 600, 1000
-    q, k, v = synth.case_plain(C, P, 5400)
-    kp, vp, table = synth.to_pages(k, v, 16, 5401)
+    contiguous path bit for bit (16-row and 32-row work items)."""
+    q, k, v = synth.case_plain(C, P, 5400 + C)
+    kp, vp, table = synth.to_pages(k, v, 16, 5401 + C)
     pp, pc = cpf.plan(C, P, paged=True), cpf.plan(C, P)
     assert pp.pop("lds_bytes") == pc.pop("lds_bytes") - 4 + 2 * 4 * pc["keys_per_tile"]   # + page-offset table
     assert pp == pc
