@@ -1113,7 +1113,7 @@ naive_pv_kernel(const float* __restrict__ S, const float* __restrict__ v, float*
 // ---------------------------------------------------------------------------
 // Host side: argument checks, launch plan, dispatch.
 // ---------------------------------------------------------------------------
-enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3, kV_decode = 4 };
+enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3, kV_decode = 4, kV_8x2 = 5 };
 
 struct Plan {
     int rows, ks, grid, threads, per_wg, bk, lds, variant, n_row_tiles, paired;
@@ -1139,15 +1139,21 @@ Plan make_plan(int C, int variant) {
     return p;
 }
 
-// Long chunks: 32 rows x 4 heads per work item; fp32 splits each 128-key tile
-// over 4 waves (16-wave workgroups, 4 waves per SIMD), bf16 over 2 (its LDS
-// and registers allow two 8-wave workgroups per CU).  Medium chunks: 16 rows,
-// 4 key splits.  Short chunks: 8 rows, 4 key splits.
+// Long chunks: fp32 takes 32 rows x 4 heads per work item and splits each
+// 128-key tile over 4 waves (16-wave workgroups, 4 waves per SIMD); bf16 splits
+// 64-key tiles over 2 waves, with 64 rows per work item (16 waves) from 4096
+// rows on, where row tiles still pair into 256 workgroups (each staged tile
+// then serves twice the queries: ~3% faster on long prefixes, whose K/V exceed
+// the L2), and 32 rows (8-wave workgroups, two per CU) below that or for paged
+// caches.  Medium chunks: 16 rows, 4 key splits.
+// Short chunks: 8 rows, 4 key splits.
 template <typename T>
 Plan choose_plan(int C, bool paged) {
     // (the paged fp32 16-wave kernel spills a few registers outside its key loop
     // and is still ~3% faster than the 8-wave one)
-    Plan p = C >= 1024 ? (sizeof(T) == 4 ? make_plan<T, 4, 4>(C, kV_4x4) : make_plan<T, 4, 2>(C, kV_4x2))
+    Plan p = C >= 1024 ? (sizeof(T) == 4              ? make_plan<T, 4, 4>(C, kV_4x4)
+                          : C >= 4096 && !paged      ? make_plan<T, 8, 2>(C, kV_8x2)
+                                                     : make_plan<T, 4, 2>(C, kV_4x2))
              : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4)
                         : make_plan<T, 1, 4>(C, kV_1x4);
     p.lds += 4 * (paged ? 2 * p.bk : 1);   // the page-offset table (one word when unused)
@@ -1178,6 +1184,9 @@ hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, 
             if constexpr (MODE == kSplit) return hipErrorInvalidValue;   // never planned
             else return launch<T, 4, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
         case kV_2x4: return launch<T, 2, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
+        case kV_8x2:   // planned for bf16 contiguous caches only
+            if constexpr (MODE != kPlain || sizeof(T) != 2) return hipErrorInvalidValue;
+            else return launch<T, 8, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
         case kV_4x4:   // planned for fp32 only, never with key splits
             if constexpr (MODE == kSplit || sizeof(T) != 4) return hipErrorInvalidValue;
             else return launch<T, 4, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);

@@ -147,10 +147,13 @@ def test_paged_validate_codes():
     assert pv(out=A + 64 * MB, kp=A + 64 * MB) == ALIAS
 
 
-def test_long_chunks_use_the_16_wave_fp32_kernel_paged_or_not():
+def test_long_chunk_workgroup_shapes():
     for paged in (False, True):
-        assert cpf.plan(2048, 2048, paged=paged)["threads"] == 1024
+        assert cpf.plan(2048, 2048, paged=paged)["threads"] == 1024          # fp32: 32 rows, 16 waves
         assert cpf.plan(2048, 2048, dtype=torch.bfloat16, paged=paged)["threads"] == 512
+    bf = cpf.plan(4096, 28672, dtype=torch.bfloat16)                        # bf16: 64 rows, paired
+    assert (bf["rows_per_item"], bf["threads"], bf["grid"], bf["items_per_workgroup"]) == (64, 1024, 256, 2)
+    assert cpf.plan(4096, 28672, dtype=torch.bfloat16, paged=True)["rows_per_item"] == 32
 
 
 def test_splitkv_workspace_sizes():
