@@ -41,6 +41,8 @@ WORKLOADS = {
                         "fp32 long cached prefix C=512 at P=15872 (16384 KV positions), last key of KV head 0 "
                         "planted at 4.0"),
     "t2048_p0_f32": (2048, 0, "f32", 300, "fp32 plain causal prompt prefill T=2048, P=0"),
+    "t1024_p0_f32": (1024, 0, "f32", 310, "fp32 plain causal prompt prefill T=1024, P=0"),
+    "t512_p0_f32": (512, 0, "f32", 320, "fp32 plain causal prompt prefill T=512, P=0"),
     "c4096_p28672_bf16": (4096, 28672, "bf16", 500,
                           "bf16 q/k/v, fp32 accumulation and output, C=4096 at P=28672 (32768 KV positions)"),
     "c1_p16383_f32_splitkv": (1, 16383, "f32", 800,

@@ -1120,8 +1120,10 @@ struct Plan {
     int splits, split_len;   // key-range splits across workgroups (0: none)
 };
 
+// pair < 0: pair tiles i and n-1-i when that still leaves a workgroup per CU;
+// otherwise pair iff pair != 0.
 template <typename T, int NW, int KS>
-Plan make_plan(int C, int variant) {
+Plan make_plan(int C, int variant, int pair = -1) {
     using G = Geo<T, NW, KS>;
     Plan p{};
     p.rows = G::kRows;
@@ -1131,37 +1133,68 @@ Plan make_plan(int C, int variant) {
     p.lds = G::kLdsBytes;
     p.variant = variant;
     p.n_row_tiles = (C + G::kRows - 1) / G::kRows;
-    // Pair tiles i and n-1-i when that still leaves a workgroup per CU.
     const int pairs = (p.n_row_tiles + 1) / 2;
-    p.paired = pairs * kHKV >= 256 ? 1 : 0;
+    p.paired = pair < 0 ? (pairs * kHKV >= 256 ? 1 : 0) : (pair != 0);
     p.per_wg = p.paired ? 2 : 1;
     p.grid = (p.paired ? pairs : p.n_row_tiles) * kHKV;
     return p;
 }
 
-// Long chunks: fp32 takes 32 rows x 4 heads per work item and splits each
-// 128-key tile over 4 waves (16-wave workgroups, 4 waves per SIMD); bf16 splits
-// 64-key tiles over 2 waves, with 64 rows per work item (16 waves) from 4096
-// rows on, where row tiles still pair into 256 workgroups (each staged tile
-// then serves twice the queries: ~3% faster on long prefixes, whose K/V exceed
-// the L2), and 32 rows (8-wave workgroups, two per CU) below that or for paged
-// caches.  Medium chunks: 16 rows, 4 key splits.
-// Short chunks: 8 rows, 4 key splits.
+// Makespan estimate for fp32 work items of H rows (every fp32 shape takes
+// 128 KiB of LDS, so a CU runs one workgroup at a time).  An item of H rows over
+// k keys costs H*k/eff + kItemCost, eff the shape's measured relative efficiency
+// and kItemCost the fixed cost of an item (Q load, first tile, merge and stores:
+// about 3 us, the time a 32-row item spends on 52 keys).  Unpaired workgroups
+// are launched heaviest first, so their makespan is about the larger of the
+// heaviest item and the mean load per CU; paired ones (tiles i and n-1-i) all
+// cost about the same and run in ceil(workgroups/256) rounds.  The mean load is
+// what an ideal heaviest-first schedule reaches; pairing wins ties (within 2%):
+// fewer workgroups, no scheduling tail (C=2048 P=0: 4% faster).
+struct ShapeCost {
+    double t;
+    int paired;
+};
+inline ShapeCost shape_cost(int C, int P, int H, double eff) {
+    constexpr double kCUs = 256.0, kItemCost = 32.0 * 52.0;
+    const double n = (double)((C + H - 1) / H);
+    // keys of tile i: P + min(H(i+1), C); only the last tile is capped
+    const double work = (double)H * (n * P + (double)H * (n - 1) * n / 2 + C) / eff;
+    const double tu = fmax((double)H * ((double)P + C) / eff + kItemCost, (work + n * kItemCost) * kHKV / kCUs);
+    const double tp = ceil(ceil(n / 2) * kHKV / kCUs) * ((double)H * (2.0 * P + C + H) / eff + 2 * kItemCost);
+    return tp <= 1.02 * tu ? ShapeCost{tp, 1} : ShapeCost{tu, 0};
+}
+
+// fp32 (contiguous or paged): 32, 16 or 8 rows x 4 heads per work item (16-,
+// 8- or 4-wave workgroups, 4 key-split waves over 128-key tiles), paired or
+// not, whichever the estimate above makes fastest (relative efficiencies 1,
+// 0.92, 0.68, measured on balanced grids).  Long chunks take 32 rows in pairs;
+// a short prompt (P small against C) takes smaller items so that causal work
+// evens out over the CUs (C=1024 at P=0: 1.5x the throughput of unpaired
+// 32-row items).  bf16: 64-key tiles over 2 waves, 64 rows per work item (16
+// waves) from 4096 rows on, where row tiles still pair into 256 workgroups
+// (each staged tile then serves twice the queries: ~3% faster on long
+// prefixes, whose K/V exceed the L2), 32 rows (8-wave workgroups, two per CU)
+// from 1024 rows or for paged caches, then 16 and 8 rows.
 template <typename T>
-Plan choose_plan(int C, bool paged) {
-    // (the paged fp32 16-wave kernel spills a few registers outside its key loop
-    // and is still ~3% faster than the 8-wave one)
-    Plan p = C >= 1024 ? (sizeof(T) == 4              ? make_plan<T, 4, 4>(C, kV_4x4)
-                          : C >= 4096 && !paged      ? make_plan<T, 8, 2>(C, kV_8x2)
-                                                     : make_plan<T, 4, 2>(C, kV_4x2))
-             : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4)
-                        : make_plan<T, 1, 4>(C, kV_1x4);
+Plan choose_plan(int C, int P, bool paged) {
+    Plan p;
+    if constexpr (sizeof(T) == 4) {
+        const ShapeCost c32 = shape_cost(C, P, 32, 1.0), c16 = shape_cost(C, P, 16, 0.92),
+                        c8 = shape_cost(C, P, 8, 0.68);
+        if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired);
+        else if (c16.t <= c8.t) p = make_plan<T, 2, 4>(C, kV_2x4, c16.paired);
+        else p = make_plan<T, 1, 4>(C, kV_1x4, c8.paired);
+    } else {
+        p = C >= 1024 ? (C >= 4096 && !paged ? make_plan<T, 8, 2>(C, kV_8x2) : make_plan<T, 4, 2>(C, kV_4x2))
+            : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4)
+                       : make_plan<T, 1, 4>(C, kV_1x4);
+    }
     p.lds += 4 * (paged ? 2 * p.bk : 1);   // the page-offset table (one word when unused)
     return p;
 }
 
-Plan plan_for(int C, attn_dtype_t dtype, bool paged) {
-    return dtype == ATTN_DTYPE_BF16 ? choose_plan<__bf16>(C, paged) : choose_plan<float>(C, paged);
+Plan plan_for(int C, int P, attn_dtype_t dtype, bool paged) {
+    return dtype == ATTN_DTYPE_BF16 ? choose_plan<__bf16>(C, P, paged) : choose_plan<float>(C, P, paged);
 }
 
 template <typename T, int NW, int KS, int MODE>
@@ -1277,7 +1310,7 @@ attn_status_t attn_prefill_plan(int C, int P, attn_dtype_t dtype, int paged, int
     if (!plan) return ATTN_ERR_NULL_PTR;
     if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
     if (C < 0 || P < 0 || P > INT_MAX - C) return ATTN_ERR_INVALID_ARG;
-    const Plan p = plan_for(C > 0 ? C : 1, dtype, paged != 0);
+    const Plan p = plan_for(C > 0 ? C : 1, P, dtype, paged != 0);
     plan[0] = p.rows;
     plan[1] = p.ks;
     plan[2] = C > 0 ? p.grid : 0;
@@ -1293,7 +1326,7 @@ attn_status_t attn_prefill(const void* q, const void* kCache, const void* vCache
                            attn_dtype_t dtype, hipStream_t stream) {
     const attn_status_t st = attn_prefill_validate(q, kCache, vCache, out, C, P, dtype);
     if (st != ATTN_OK || C == 0) return st;
-    const Plan p = plan_for(C, dtype, false);
+    const Plan p = plan_for(C, P, dtype, false);
     const PagedCache none{nullptr, 1, 0};
     const KeySplit nosplit{nullptr, 0, 0};
     const hipError_t e = dtype == ATTN_DTYPE_BF16
@@ -1448,7 +1481,7 @@ attn_status_t attn_prefill_paged(const void* q, const void* kPages, const void* 
     const attn_status_t st =
         attn_prefill_paged_validate(q, kPages, vPages, blockTable, numBlocks, pageSize, out, C, P, dtype);
     if (st != ATTN_OK || C == 0) return st;
-    const Plan p = plan_for(C, dtype, true);
+    const Plan p = plan_for(C, P, dtype, true);
     const PagedCache pg{blockTable, pageSize, numBlocks};
     const KeySplit nosplit{nullptr, 0, 0};
     const hipError_t e = dtype == ATTN_DTYPE_BF16

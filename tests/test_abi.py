@@ -147,6 +147,18 @@ def test_paged_validate_codes():
     assert pv(out=A + 64 * MB, kp=A + 64 * MB) == ALIAS
 
 
+def test_fp32_plans_balance_causal_work():
+    """Row-tile height and pairing per shape (see the planner's makespan
+    estimate): (rows per item, workgroups, items per workgroup)."""
+    want = {(2048, 2048): (32, 256, 2), (2048, 0): (32, 256, 2), (512, 15872): (16, 256, 1),
+            (1024, 0): (16, 256, 2), (1536, 0): (16, 768, 1), (512, 0): (8, 256, 2), (600, 0): (16, 304, 1),
+            (255, 3): (8, 256, 1), (1000, 13): (16, 256, 2), (1500, 100): (16, 752, 1), (2049, 7): (32, 520, 1),
+            (17, 31): (8, 24, 1)}
+    for (C, P), w in want.items():
+        p = cpf.plan(C, P)
+        assert (p["rows_per_item"], p["grid"], p["items_per_workgroup"]) == w, (C, P, p)
+
+
 def test_long_chunk_workgroup_shapes():
     for paged in (False, True):
         assert cpf.plan(2048, 2048, paged=paged)["threads"] == 1024          # fp32: 32 rows, 16 waves
