@@ -1140,11 +1140,12 @@ Plan make_plan(int C, int variant, int pair = -1) {
     return p;
 }
 
-// Makespan estimate for fp32 work items of H rows (every fp32 shape takes
-// 128 KiB of LDS, so a CU runs one workgroup at a time).  An item of H rows over
-// k keys costs H*k/eff + kItemCost, eff the shape's measured relative efficiency
-// and kItemCost the fixed cost of an item (Q load, first tile, merge and stores:
-// about 3 us, the time a 32-row item spends on 52 keys).  Unpaired workgroups
+// Makespan estimate for work items of H rows where a CU runs one workgroup at a
+// time (every fp32 shape takes 128 KiB of LDS; the 64-row bf16 shape 16 waves).
+// An item of H rows over k keys costs H*k/eff + item, eff the shape's measured
+// relative efficiency and item the fixed cost of an item (Q load, first tile,
+// merge and stores: about 3 us, the time a 32-row fp32 item spends on 52 keys
+// and a 64-row bf16 item on 177).  Unpaired workgroups
 // are launched heaviest first, so their makespan is about the larger of the
 // heaviest item and the mean load per CU; paired ones (tiles i and n-1-i) all
 // cost about the same and run in ceil(workgroups/256) rounds.  The mean load is
@@ -1154,13 +1155,13 @@ struct ShapeCost {
     double t;
     int paired;
 };
-inline ShapeCost shape_cost(int C, int P, int H, double eff) {
-    constexpr double kCUs = 256.0, kItemCost = 32.0 * 52.0;
+inline ShapeCost shape_cost(int C, int P, int H, double eff, double item) {
+    constexpr double kCUs = 256.0;
     const double n = (double)((C + H - 1) / H);
     // keys of tile i: P + min(H(i+1), C); only the last tile is capped
     const double work = (double)H * (n * P + (double)H * (n - 1) * n / 2 + C) / eff;
-    const double tu = fmax((double)H * ((double)P + C) / eff + kItemCost, (work + n * kItemCost) * kHKV / kCUs);
-    const double tp = ceil(ceil(n / 2) * kHKV / kCUs) * ((double)H * (2.0 * P + C + H) / eff + 2 * kItemCost);
+    const double tu = fmax((double)H * ((double)P + C) / eff + item, (work + n * item) * kHKV / kCUs);
+    const double tp = ceil(ceil(n / 2) * kHKV / kCUs) * ((double)H * (2.0 * P + C + H) / eff + 2 * item);
     return tp <= 1.02 * tu ? ShapeCost{tp, 1} : ShapeCost{tu, 0};
 }
 
@@ -1174,19 +1175,24 @@ inline ShapeCost shape_cost(int C, int P, int H, double eff) {
 // waves) from 4096 rows on, where row tiles still pair into 256 workgroups
 // (each staged tile then serves twice the queries: ~3% faster on long
 // prefixes, whose K/V exceed the L2), 32 rows (8-wave workgroups, two per CU)
-// from 1024 rows or for paged caches, then 16 and 8 rows.
+// from 2048 rows or for paged caches, then 16 rows unpaired (C=1024: 7% faster
+// than 32 rows at P=0, 13% at P=1024) and 8 rows below 256.
 template <typename T>
 Plan choose_plan(int C, int P, bool paged) {
     Plan p;
     if constexpr (sizeof(T) == 4) {
-        const ShapeCost c32 = shape_cost(C, P, 32, 1.0), c16 = shape_cost(C, P, 16, 0.92),
-                        c8 = shape_cost(C, P, 8, 0.68);
+        constexpr double kItem = 32.0 * 52.0;
+        const ShapeCost c32 = shape_cost(C, P, 32, 1.0, kItem), c16 = shape_cost(C, P, 16, 0.92, kItem),
+                        c8 = shape_cost(C, P, 8, 0.68, kItem);
         if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired);
         else if (c16.t <= c8.t) p = make_plan<T, 2, 4>(C, kV_2x4, c16.paired);
         else p = make_plan<T, 1, 4>(C, kV_1x4, c8.paired);
     } else {
-        p = C >= 1024 ? (C >= 4096 && !paged ? make_plan<T, 8, 2>(C, kV_8x2) : make_plan<T, 4, 2>(C, kV_4x2))
-            : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4)
+        // two 16-row workgroups fit a CU, so pairing them into 256 workgroups
+        // would leave half the slots empty: they stay unpaired
+        p = C >= 2048 ? (C >= 4096 && !paged ? make_plan<T, 8, 2>(C, kV_8x2, shape_cost(C, P, 64, 1.0, 64.0 * 177.0).paired)
+                                             : make_plan<T, 4, 2>(C, kV_4x2))
+            : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4, 0)
                        : make_plan<T, 1, 4>(C, kV_1x4);
     }
     p.lds += 4 * (paged ? 2 * p.bk : 1);   // the page-offset table (one word when unused)
