@@ -187,3 +187,36 @@ def to_pages(k: np.ndarray, v: np.ndarray, page_size: int, seed: int, spare_page
         kp[table[b], : hi - lo] = k[lo:hi]
         vp[table[b], : hi - lo] = v[lo:hi]
     return kp, vp, table
+
+
+def case_long_cache(C: int, P: int, seed_base: int = 1100, k_scale: float = 6.0, band: int = 4096):
+    """A cache too long to fill with i.i.d. draws cheaply (P+C positions,
+    typically past 2^20 so fp32 byte offsets pass 2^31).
+
+    q is i.i.d. N(0,1).  Three bands of positions hold i.i.d. draws, K scaled
+    by k_scale so their scores dominate the softmax: [0, band), `band`
+    positions centred on position 2^20 (the first position whose fp32 K/V
+    rows start at byte 2^31), and the last 2*band positions (the chunk and
+    the keys just before it).  Elsewhere K is zero (score 0) and V repeats a
+    17-position pattern of multiples of 1/8 in [-1, 1]; 2^20 is not a
+    multiple of 17, so a row read from a wrapped offset differs."""
+    T = P + C
+    q = normal_f32(seed_base + 1, C * HQ * D).reshape(C, HQ, D)
+    k = np.zeros((T, HKV, D), dtype=np.float32)
+    period = 17
+    j = np.arange(period, dtype=np.int64)[:, None, None]
+    g = np.arange(HKV, dtype=np.int64)[None, :, None]
+    d = np.arange(D, dtype=np.int64)[None, None, :]
+    pattern = (((5 * j + 3 * g + d) % 17) - 8).astype(np.float32) / 8.0
+    v = pattern[np.arange(T, dtype=np.int64) % period]
+    mid = 1 << 20
+    bands = [(0, band), (mid - band // 2, mid + band // 2), (T - 2 * band, T)]
+    for t, (lo, hi) in enumerate(bands):
+        lo, hi = max(0, lo), min(T, hi)
+        if hi <= lo:
+            continue
+        n = (hi - lo) * HKV * D
+        k[lo:hi] = (k_scale * normal_f32(seed_base + 2 + 10 * t, n).astype(np.float64)).astype(
+            np.float32).reshape(hi - lo, HKV, D)
+        v[lo:hi] = normal_f32(seed_base + 3 + 10 * t, n).reshape(hi - lo, HKV, D)
+    return q, k, v, bands
