@@ -97,12 +97,12 @@ def traffic_entry(name):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(name, q, k, v, P, dt, budget_s=12.0):
+def cpu_baseline(name, q, k, v, P, dt, budget_s=15.0, min_s=10.0):
     """Time the CPU oracle, on all the host threads OpenMP gives it.
 
     The whole workload is run when a short trial predicts it fits the budget
-    (repeated up to 3 times while it does); otherwise an evenly spaced sample
-    of rows (all 32 heads each) sized to the budget.  The value counts the
+    (repeated until about min_s seconds of work, within the budget); otherwise
+    an evenly spaced sample of rows (all 32 heads each) sized to the budget.  The value counts the
     same 4*d FLOPs per visible pair as the GPU figure, over what was run."""
     import numpy as np
     import oracle
@@ -133,7 +133,8 @@ def cpu_baseline(name, q, k, v, P, dt, budget_s=12.0):
             t0 = time.perf_counter()
             oracle.attn_prefill(q, k, v, P)
             times.append(time.perf_counter() - t0)
-            if len(times) >= 3 or time.perf_counter() - t_all + times[-1] > budget_s:
+            elapsed = time.perf_counter() - t_all
+            if elapsed >= min_s or elapsed + times[-1] > budget_s:
                 break
         per = float(np.mean(times))
         return {"value": round(full / per / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
