@@ -149,7 +149,10 @@ def cpu_baseline(name, q, k, v, P, dt, budget_s=15.0, min_s=10.0):
 
 
 def sampled_parity(got, q, k, v, P, dt):
-    """Spot-check the benchmarked output against the oracle on 8 rows."""
+    """Spot-check the benchmarked output against the oracle on 8 rows (all
+    heads).  Returns (all within tolerance, error statistics): max absolute,
+    max relative (over |ref| >= 1e-3), RMS, and the largest error as a fraction
+    of its element's tolerance."""
     import numpy as np
     import oracle
     import synth
@@ -166,7 +169,11 @@ def sampled_parity(got, q, k, v, P, dt):
     else:
         tol = 1e-5 + 2.0 ** -8 * oracle.attn_rows(q, k, np.abs(v), P, rr, hh).astype(np.float64)
     err = np.abs(g - ref)
-    return bool(np.all(err <= tol)), float(err.max())
+    big = np.abs(ref) >= 1e-3
+    stats = {"sampled_rows": int(len(rows)), "max_abs_err": float(err.max()),
+             "max_rel_err": float((err[big] / np.abs(ref[big])).max()) if big.any() else None,
+             "rms_err": float(np.sqrt(np.mean(err ** 2))), "worst_err_over_tol": float((err / tol).max())}
+    return bool(np.all(err <= tol)), stats
 
 
 def main():
@@ -238,9 +245,9 @@ def main():
         if n_w % 10 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    ok, maxerr = (True, None) if args.no_check else sampled_parity(out.cpu().numpy(), q, k, v, P, dt)
+    ok, errstats = (True, None) if args.no_check else sampled_parity(out.cpu().numpy(), q, k, v, P, dt)
     if not ok:
-        print("bench: sampled parity check FAILED (max err %g)" % maxerr, file=sys.stderr)
+        print("bench: sampled parity check FAILED (%s)" % json.dumps(errstats), file=sys.stderr)
         sys.exit(1)
 
     # timed region: K steps, synchronised on both sides; HIP events on the
@@ -322,7 +329,7 @@ def main():
                      "kernel": KERNEL_NAME, "kernel_ms": round(kernel_ms, 5)},
         "launch_ms": launch_ms,
         "cold_launch_ms": cold_ms,
-        "parity": {"sampled_rows_ok": ok, "max_abs_err": maxerr},
+        "parity": dict({"sampled_rows_ok": ok}, **(errstats or {})),
     }
     esz = 4 if dt == "f32" else 2
     alg_bytes = C * 32 * 64 * esz + 2 * (P + C) * 8 * 64 * esz + C * 32 * 64 * 4
