@@ -48,6 +48,9 @@ WORKLOADS = {
     "c1_p16383_f32_splitkv": (1, 16383, "f32", 800,
                               "fp32 decode: one token at P=16383 (16384 KV positions), key range split across "
                               "workgroups and merged; q/k/v i.i.d. N(0,1)"),
+    "c1_p131071_f32_splitkv": (1, 131071, "f32", 820,
+                               "fp32 decode: one token at P=131071 (131072 KV positions, 512 MiB of K/V, more "
+                               "than the 256 MB Infinity Cache holds), split across workgroups"),
     "c1_p32767_bf16_splitkv": (1, 32767, "bf16", 810,
                                "bf16 decode: one token at P=32767 (32768 KV positions), split across workgroups"),
     "c2048_p2048_f32_paged16": (2048, 2048, "f32", 200,
