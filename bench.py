@@ -200,7 +200,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -1,5 +1,6 @@
 """bench.py's command-line contract, checked without a GPU: more than one GPU
-is refused with a message (this build measures one GPU only)."""
+is refused with a message (the library runs on one GPU), and every workload
+is listed."""
 import os
 import subprocess
 import sys
@@ -19,5 +20,6 @@ def test_help_lists_the_workloads():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0
-    for w in ("c2048_p2048_f32", "c4096_p28672_bf16", "c1_p16383_f32_splitkv", "c2048_p2048_f32_paged16"):
+    for w in ("c2048_p2048_f32", "c4096_p28672_bf16", "c1_p16383_f32_splitkv", "c1_p131071_f32_splitkv",
+              "c2048_p2048_f32_paged16"):
         assert w in r.stdout
