@@ -10,6 +10,7 @@ in four).  Inputs carry three 4.0 plants in the chunk, which must come out
 as exactly 4.0.  Tolerances as in test_parity_gpu.py.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -87,3 +88,55 @@ def test_shape(entry, dtype, C, P, page):
         pytest.fail("%d of %d out of tolerance; first %s got %r ref %r" % (bad.sum(), bad.size, i, got[i], ref[i]))
     for p in plants:
         assert np.all(got[p - P, 0] == 4.0), "planted row %d" % (p - P)
+
+
+def test_wide_sweep_sampled_rows():
+    """A wider seeded sweep checked on sampled rows (first, last, six drawn, the
+    planted ones; all 32 heads): entry point among contiguous, paged (pages of
+    1-256 positions), split-KV and per-row; C log-uniform in [1, 2500], P in
+    [0, 6000] (0 one time in five).  CPF_SWEEP_CASES sets the number of cases
+    (default 200, a few seconds; 3000 take under two minutes)."""
+    n = int(os.environ.get("CPF_SWEEP_CASES", "200"))
+    r = synth.uniform53(778, 8 * n)
+    bad = []
+    for t in range(n):
+        u = r[8 * t: 8 * t + 8]
+        entry = ("prefill", "paged", "splitkv", "rowwise")[int(u[0] * 4) % 4]
+        dtype = "bf16" if u[1] < 0.5 else "f32"
+        C = max(1, int(round(math.exp(u[2] * math.log(2500)))))
+        P = 0 if u[3] < 0.2 else int(round(math.exp(u[4] * math.log(6000))))
+        page = (1, 2, 7, 16, 31, 64, 100, 128, 256)[int(u[5] * 9) % 9]
+        if entry == "rowwise" and C * (P + C) > 3e6:
+            entry = "prefill"   # the per-row baseline is slow on big shapes
+        seed = 50000 + t
+        q, k, v, plants = synth.case_planted_chunk(C, P, seed, 3)
+        tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+        out = torch.full((C, HQ, D), float("nan"), device="cuda")
+        if entry == "prefill":
+            cpf.attn_prefill(_gpu(q, dtype), _gpu(k, dtype), _gpu(v, dtype), out=out, P=P)
+        elif entry == "rowwise":
+            cpf.attn_prefill_rowwise(_gpu(q, dtype), _gpu(k, dtype), _gpu(v, dtype), out=out, P=P)
+        elif entry == "paged":
+            kp, vp, table = synth.to_pages(k, v, page, seed + 5)
+            cpf.attn_prefill_paged(_gpu(q, dtype), _gpu(kp, dtype), _gpu(vp, dtype),
+                                   torch.from_numpy(table).cuda(), P, out=out)
+        else:
+            need, _ = cpf.splitkv_workspace(C, P, tdt)
+            ws = torch.full((need // 4 + 4,), float("nan"), device="cuda")
+            cpf.attn_prefill_splitkv(_gpu(q, dtype), _gpu(k, dtype), _gpu(v, dtype), out=out, P=P, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        rows = sorted(set([0, C - 1] + [int(x * C) % C for x in synth.uniform53(seed + 9, 6)] + [p - P for p in plants]))
+        rr = np.repeat(np.array(rows, dtype=np.int32), HQ)
+        hh = np.tile(np.arange(HQ, dtype=np.int32), len(rows))
+        qo, ko, vo = _widen(q, dtype), _widen(k, dtype), _widen(v, dtype)
+        ref = oracle.attn_rows(qo, ko, vo, P, rr, hh).astype(np.float64)
+        if dtype == "f32":
+            tol = 1e-4 + 1e-3 * np.abs(ref)
+        else:
+            tol = 1e-5 + 2.0 ** -8 * oracle.attn_rows(qo, ko, np.abs(vo), P, rr, hh).astype(np.float64)
+        ok = bool(np.all(np.abs(got[rr, hh] - ref) <= tol)) and bool(np.isfinite(got).all())
+        ok = ok and all(bool(np.all(got[p - P, 0] == 4.0)) for p in plants)
+        if not ok:
+            bad.append((t, entry, dtype, C, P, page))
+    assert not bad, "%d of %d cases failed, first %s" % (len(bad), n, bad[:5])
