@@ -22,6 +22,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +62,108 @@ DEFAULT = "c2048_p2048_f32"
 KERNEL_NAME = "attn_prefill_kernel"
 KERNEL_SRC = os.path.join(ROOT, "chunked_prefill_flash_amd", "csrc", "attn_prefill.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+NOMINAL_MHZ = 2400.0   # the clock the published peaks assume
+
+
+class ClockSampler:
+    """Samples the shader (gfx) clock in a background thread while the timed
+    region runs: the per-XCD current_gfxclks of the SMU metrics table, read
+    in-process through the amdsmi library (no subprocess), every `period_s`.
+    Each sample is the mean over the XCDs.  If amdsmi is missing or the
+    device does not expose the metrics, `summary()` says why instead."""
+
+    def __init__(self, period_s=0.002, lead_s=0.25):
+        self.lead_s = lead_s
+        self.period_s = period_s
+        self.samples = []          # (host time, MHz)
+        self.window = None         # host times bounding the timed region
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        self._amdsmi = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                raise RuntimeError("no GPU handles")
+            self._handle = self._match(amdsmi, handles)
+            self._amdsmi = amdsmi
+            self._read()
+        except Exception as exc:   # no clock reading: reported, never fatal
+            self.error = "%s: %s" % (type(exc).__name__, exc)
+
+    @staticmethod
+    def _match(amdsmi, handles):
+        """The handle whose PCI address is cuda:0's (the first one otherwise)."""
+        try:
+            import torch
+            pr = torch.cuda.get_device_properties(0)
+            want = "%04x:%02x:%02x" % (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
+            for h in handles:
+                if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want):
+                    return h
+        except Exception:
+            pass
+        return handles[0]
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+        if not clks:
+            c = m.get("current_gfxclk")
+            if not isinstance(c, (int, float)):
+                raise RuntimeError("gpu metrics hold no current gfx clock")
+            clks = [c]
+        return sum(clks) / len(clks)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append((time.perf_counter(), self._read()))
+            except Exception as exc:
+                self.error = "%s: %s" % (type(exc).__name__, exc)
+                return
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        if self._amdsmi is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        if self._amdsmi is not None:
+            try:
+                self._amdsmi.amdsmi_shut_down()
+            except Exception:
+                pass
+
+    def mark(self, t0, t1):
+        """The timed region ran from host time t0 to t1."""
+        self.window = (t0, t1)
+
+    def summary(self):
+        """Samples from lead_s before the timed region to its end (the metrics
+        table refreshes every few tens of ms, so the lead keeps a short timed
+        region from reading only values taken before it, under the same
+        back-to-back load of the warmup)."""
+        xs = self.samples
+        if self.window:
+            xs = [s for s in xs if self.window[0] - self.lead_s <= s[0] <= self.window[1]]
+        if not xs:
+            return {"median_mhz": None, "samples": 0, "error": self.error or "no samples"}
+        ys = sorted(m for _, m in xs)
+        return {"median_mhz": round(ys[len(ys) // 2], 1), "min_mhz": round(ys[0], 1), "max_mhz": round(ys[-1], 1),
+                "samples": len(ys), "period_ms": self.period_s * 1e3,
+                "source": "amdsmi gpu_metrics current_gfxclks, mean over XCDs, sampled in another thread from "
+                          "%.2f s before the timed steps (the warmup's back-to-back calls) to their end"
+                          % self.lead_s}
 
 
 def kernel_source_hash() -> str:
@@ -194,6 +297,7 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time 20 calls each preceded by a 1 GiB read, so inputs come from HBM "
                          "rather than the 256 MB Infinity Cache")
+    ap.add_argument("--no-clock", action="store_true", help="do not sample the shader clock")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB three times "
                          "(reference kernel of known traffic for HBM byte counters)")
@@ -240,6 +344,19 @@ def main():
         else:
             cpf.attn_prefill(qd, kd, vd, out=out, P=P, stream=stream)
 
+    # the output of a first call is checked against the oracle on the CPU
+    # before the warmup, so that the GPU does not sit idle (and its clock drop)
+    # between the warmup and the timed steps
+    call()
+    torch.cuda.synchronize()
+    ok, errstats = (True, None) if args.no_check else sampled_parity(out.cpu().numpy(), q, k, v, P, dt)
+    if not ok:
+        print("bench: sampled parity check FAILED (%s)" % json.dumps(errstats), file=sys.stderr)
+        sys.exit(1)
+    clock = ClockSampler() if not args.no_clock else None
+    if clock:
+        clock.start()
+
     t_w = time.perf_counter()
     n_w = 0
     while n_w < max(args.warmup, 1) or time.perf_counter() - t_w < args.warmup_seconds:
@@ -247,14 +364,10 @@ def main():
         n_w += 1
         if n_w % 10 == 0:
             torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    ok, errstats = (True, None) if args.no_check else sampled_parity(out.cpu().numpy(), q, k, v, P, dt)
-    if not ok:
-        print("bench: sampled parity check FAILED (%s)" % json.dumps(errstats), file=sys.stderr)
-        sys.exit(1)
 
     # timed region: K steps, synchronised on both sides; HIP events on the
-    # stream the kernel is launched on give the per-launch device time
+    # stream the kernel is launched on give the per-launch device time; the
+    # shader clock is sampled meanwhile from another thread
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -264,7 +377,11 @@ def main():
         call()
     ev1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    if clock:
+        clock.stop()
+        clock.mark(t0, t1)
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
@@ -331,9 +448,15 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic_entry(name),
                      "kernel": KERNEL_NAME, "kernel_ms": round(kernel_ms, 5)},
         "launch_ms": launch_ms,
+        "clock": clock.summary() if clock else None,
         "cold_launch_ms": cold_ms,
         "parity": dict({"sampled_rows_ok": ok}, **(errstats or {})),
     }
+    if clock and result["clock"].get("median_mhz"):
+        # the same fraction against the peak at the clock the chip ran at
+        mhz = result["clock"]["median_mhz"]
+        result["roofline"]["peak_at_clock"] = round(peak * mhz / NOMINAL_MHZ, 2)
+        result["roofline"]["frac_at_clock"] = round(achieved / (peak * mhz / NOMINAL_MHZ), 4)
     esz = 4 if dt == "f32" else 2
     alg_bytes = C * 32 * 64 * esz + 2 * (P + C) * 8 * 64 * esz + C * 32 * 64 * 4
     if splitkv:
@@ -360,8 +483,9 @@ def main():
         base_ms = e0.elapsed_time(e1) / n_base
         result["speedup_vs_rowwise"] = {"rowwise_ms": round(base_ms, 4), "tiled_ms": round(kernel_ms, 5),
                                         "speedup": round(base_ms / kernel_ms, 2),
-                                        "baseline": "per-row online softmax, one (row, head) per 32 lanes, "
-                                                    "every row re-reads its prefix (the pages' starter)"}
+                                        "baseline": "per-row kernel with no tiling: one (row, head) per wave, scores lane per key, "
+                                                    "weighted sum lane per dim, every row streams its whole prefix "
+                                                    "(the pages' starter)"}
     if not args.no_speedup and P == 0 and dt == "f32" and not paged and not splitkv:
         # the three-kernel pipeline with the full score matrix on the same prompt
         need = cpf.naive_workspace(C)

@@ -102,10 +102,12 @@ def _gpu_tensors(device, **tensors):
             raise ValueError("%s is on %s, expected %s (all tensors on one device)" % (name, t.device, device))
 
 
-def _out_tensor(out, C: int, device) -> torch.Tensor:
-    """The caller's out (checked) or a new float32 [C][32][64] on `device`."""
+def _out_tensor(out, C: int, device, stream) -> torch.Tensor:
+    """The caller's out (checked) or a new float32 [C][32][64] on `device`,
+    allocated on `stream` (the stream the kernels write it on)."""
     if out is None:
-        return torch.empty((C, HQ, D), dtype=torch.float32, device=device)
+        with torch.cuda.stream(stream):
+            return torch.empty((C, HQ, D), dtype=torch.float32, device=device)
     if out.dtype != torch.float32 or tuple(out.shape) != (C, HQ, D):
         raise ValueError("out must be float32 [C][32][64] = [%d][32][64], got %s %s"
                          % (C, out.dtype, tuple(out.shape)))
@@ -113,11 +115,15 @@ def _out_tensor(out, C: int, device) -> torch.Tensor:
     return out
 
 
-def _workspace(workspace, need: int, device) -> torch.Tensor:
+def _workspace(workspace, need: int, device, stream) -> torch.Tensor:
     """The caller's workspace (checked for device and contiguity; the library
-    checks its size) or a new one of `need` bytes."""
+    checks its size) or a new one of `need` bytes.  A new one is allocated on
+    `stream`, the stream the kernels use it on: torch's caching allocator then
+    hands its memory to no other stream when it is freed on return, while the
+    kernels may still be running."""
     if workspace is None:
-        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
     _gpu_tensors(device, workspace=workspace)
     return workspace
 
@@ -184,8 +190,8 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
         raise ValueError("k and v must be [P+C][8][64] = [%d][8][64], got %s and %s"
                          % (P + C, tuple(k.shape), tuple(v.shape)))
     _gpu_tensors(q.device, q=q, k=k, v=v)
-    out = _out_tensor(out, C, q.device)
     s = _stream(stream, q.device)
+    out = _out_tensor(out, C, q.device, s)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = getattr(lib, _entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), C, P, DTYPES[q.dtype],
@@ -224,8 +230,8 @@ def attn_prefill_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
             block_table.shape[0] < -(-(P + C) // page_size):
         raise ValueError("block_table must be int32 with at least ceil((P+C)/pageSize) entries")
     _gpu_tensors(q.device, q=q, k_pages=k_pages, v_pages=v_pages, block_table=block_table)
-    out = _out_tensor(out, C, q.device)
     s = _stream(stream, q.device)
+    out = _out_tensor(out, C, q.device, s)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.attn_prefill_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
@@ -261,10 +267,10 @@ def attn_prefill_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out:
     if q.dim() != 3 or q.shape[1:] != (HQ, D) or k.shape != (P + C, HKV, D) or v.shape != k.shape:
         raise ValueError("bad shapes q %s k %s v %s for P=%d" % (tuple(q.shape), tuple(k.shape), tuple(v.shape), P))
     _gpu_tensors(q.device, q=q, k=k, v=v)
-    out = _out_tensor(out, C, q.device)
-    workspace = _workspace(workspace, splitkv_workspace(C, P, q.dtype)[0], q.device)
-    nbytes = workspace.numel() * workspace.element_size()
     s = _stream(stream, q.device)
+    out = _out_tensor(out, C, q.device, s)
+    workspace = _workspace(workspace, splitkv_workspace(C, P, q.dtype)[0], q.device, s)
+    nbytes = workspace.numel() * workspace.element_size()
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.attn_prefill_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), C, P, DTYPES[q.dtype],
@@ -293,10 +299,10 @@ def attn_naive(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Ten
     if q.shape != (T, HQ, D) or k.shape != (T, HKV, D) or v.shape != k.shape:
         raise ValueError("q [T][32][64], k and v [T][8][64] expected")
     _gpu_tensors(q.device, q=q, k=k, v=v)
-    out = _out_tensor(out, T, q.device)
-    workspace = _workspace(workspace, naive_workspace(T), q.device)
-    nbytes = workspace.numel() * workspace.element_size()
     s = _stream(stream, q.device)
+    out = _out_tensor(out, T, q.device, s)
+    workspace = _workspace(workspace, naive_workspace(T), q.device, s)
+    nbytes = workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
         st = load_library().attn_naive(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), T,
                                        workspace.data_ptr(), nbytes, s.cuda_stream)

@@ -706,15 +706,19 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
 }
 
 // ---------------------------------------------------------------------------
-// Per-row baseline: the algorithm of the starter in "Inference Attention 2"
-// (Starter code): no tiling, one (query row, head) per 32 lanes, each lane
-// holding 2 of the 64 dims, the dot product reduced across the 32 lanes, and
-// the online softmax (m, l, accumulator rescaled by exp(m_old - m_new))
-// updated key by key, so every row walks its whole K/V prefix through the
-// memory system on its own.  A 64-lane wave carries two adjacent rows of one
-// head; a 512-thread block covers 64 rows of one head.  It exists to be timed
-// against the tiled kernel (the page's SPEEDUP) and is checked like it.
+// Per-row baseline ("Inference Attention 2: Flash Prefill Against a Cached
+// Prefix", Lesson: the starter serves each (query row, head) on its own and
+// every row streams its whole K/V prefix from memory; nothing is staged or
+// shared between rows).  One 64-lane wave per (row, head), keys in blocks of
+// 64: for the scores lane j takes key j0 + j (its whole K row against the
+// query, which every lane holds), for the weighted sum lane d takes output dim
+// d (one coalesced V row per key, each key's weight broadcast from its lane).
+// The online softmax state moves once per block: block maximum, one rescale
+// of the denominator and accumulator, the block's weights.  The traffic per
+// row is its whole prefix, which is what the tiled kernel is timed against.
 // ---------------------------------------------------------------------------
+constexpr int kRowWaves = 4;     // waves (rows) per workgroup
+
 template <typename T>
 __device__ __forceinline__ float load_elem(const T* p) {
     if constexpr (sizeof(T) == 4) {
@@ -724,49 +728,6 @@ __device__ __forceinline__ float load_elem(const T* p) {
     }
 }
 
-template <typename T>
-__global__ void __launch_bounds__(512)
-attn_rowwise_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
-                    float* __restrict__ out, int C, int P) {
-    const int h = blockIdx.y;
-    const int g = h / kGroup;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int half = lane >> 5;        // which of the wave's two rows
-    const int d = lane & 31;           // this lane's dims: d and d + 32
-    for (int r = 0; r < 4; ++r) {
-        const int row = blockIdx.x * 64 + wave * 8 + 2 * r + half;
-        if (row >= C) break;           // a whole half-wave leaves together
-        const T* qr = q + ((size_t)row * kHQ + h) * kD;
-        const float q0 = load_elem(qr + d) * kScaleLog2;
-        const float q1 = load_elem(qr + d + 32) * kScaleLog2;
-        float m = -INFINITY, l = 0.f, a0 = 0.f, a1 = 0.f;
-        const int last = P + row;
-        for (int j = 0; j <= last; ++j) {
-            const size_t off = ((size_t)j * kHKV + g) * kD;
-            float dot = q0 * load_elem(kc + off + d) + q1 * load_elem(kc + off + d + 32);
-#pragma unroll
-            for (int o = 16; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 32);
-            const float mn = fmaxf(m, dot);
-            const float alpha = fast_exp2(m - mn);   // m = -inf on the first key: 0
-            const float p = fast_exp2(dot - mn);
-            l = alpha * l + p;
-            a0 = alpha * a0 + p * load_elem(vc + off + d);
-            a1 = alpha * a1 + p * load_elem(vc + off + d + 32);
-            m = mn;
-        }
-        float* o = out + ((size_t)row * kHQ + h) * kD;
-        o[d] = a0 / l;
-        o[d + 32] = a1 / l;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Merge of key-split partials ("FlashAttention and inference kernels",
-// Exercises, exercise 2): m = max_s m_s, w_s = 2^(m_s - m), out = sum_s w_s O_s /
-// sum_s w_s l_s over the splits a row reaches (s*len <= P + row), so no empty
-// segment takes part.  One wave per (row, head), one lane per dim.
-// ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max64(float x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
@@ -779,6 +740,81 @@ __device__ __forceinline__ float wave_sum64(float x) {
     return x;
 }
 
+// 8 consecutive elements as floats (one 16-byte load in bf16, two in fp32)
+template <typename T>
+__device__ __forceinline__ void load8f(const T* p, float (&x)[8]) {
+    if constexpr (sizeof(T) == 4) {
+        const f4 a = *reinterpret_cast<const f4*>(p);
+        const f4 b = *reinterpret_cast<const f4*>(p + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = a[e];
+            x[4 + e] = b[e];
+        }
+    } else {
+        const bf8 a = *reinterpret_cast<const bf8*>(p);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(64 * kRowWaves)
+attn_rowwise_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+                    float* __restrict__ out, int C, int P) {
+    const int lane = threadIdx.x & 63;
+    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowWaves + (threadIdx.x >> 6));
+    const int h = blockIdx.y;
+    if (row >= C) return;                              // whole waves leave together
+    const int g = h / kGroup;
+    float qv[kD];                                      // the query, scaled; the same in every lane
+    const T* qrow = q + ((size_t)row * kHQ + h) * kD;
+#pragma unroll
+    for (int c = 0; c < kD; c += 8) {
+        float x[8];
+        load8f(qrow + c, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[c + e] = x[e] * kScaleLog2;
+    }
+    constexpr size_t kPos = (size_t)kHKV * kD;         // elements between positions
+    const T* kg = kc + (size_t)g * kD;                 // KV head g at position 0
+    const T* vg = vc + (size_t)g * kD + lane;          // dim `lane` of KV head g at position 0
+    const int n = P + row + 1;                         // visible keys
+    float run_max = -INFINITY, denom = 0.f, acc = 0.f;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        const int last = n - 1 - j0;                   // lanes past it hold no key
+        const T* krow = kg + (size_t)(j0 + min(lane, last)) * kPos;
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < kD; c += 8) {
+            float x[8];
+            load8f(krow + c, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qv[c + e], x[e], s);
+        }
+        if (lane > last) s = -INFINITY;
+        const float next = fmaxf(run_max, wave_max64(s));
+        const float keep = fast_exp2(run_max - next);  // 0 on the first block (run_max = -inf)
+        const float w = fast_exp2(s - next);           // 0 for a lane with no key
+        denom = denom * keep + wave_sum64(w);
+        acc *= keep;
+        const int cnt = min(64, last + 1);
+#pragma unroll 8
+        for (int b = 0; b < 64; ++b) {                 // weights past cnt are 0; their loads stay in range
+            const float vb = load_elem(vg + (size_t)(j0 + min(b, cnt - 1)) * kPos);
+            acc = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), b)), vb, acc);
+        }
+        run_max = next;
+    }
+    out[((size_t)row * kHQ + h) * kD + lane] = acc / denom;
+}
+
+// ---------------------------------------------------------------------------
+// Merge of key-split partials ("FlashAttention and inference kernels",
+// Exercises, exercise 2): m = max_s m_s, w_s = 2^(m_s - m), out = sum_s w_s O_s /
+// sum_s w_s l_s over the splits a row reaches (s*len <= P + row), so no empty
+// segment takes part.  One wave per (row, head), one lane per dim.
+// ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 attn_merge_splits_kernel(const float* __restrict__ part, float* __restrict__ out, int C, int P, int len, int n) {
     // (row, head) index, wave-uniform: split offsets below stay scalar
@@ -1441,19 +1477,21 @@ attn_status_t attn_prefill_rowwise(const void* q, const void* kCache, const void
                                    attn_dtype_t dtype, hipStream_t stream) {
     const attn_status_t st = attn_prefill_validate(q, kCache, vCache, out, C, P, dtype);
     if (st != ATTN_OK || C == 0) return st;
-    const dim3 grid((C + 63) / 64, kHQ);
+    const dim3 grid((C + kRowWaves - 1) / kRowWaves, kHQ);
     hipError_t e;
     if (dtype == ATTN_DTYPE_BF16) {
         const __bf16 *qq = static_cast<const __bf16*>(q), *kk = static_cast<const __bf16*>(kCache),
                      *vv = static_cast<const __bf16*>(vCache);
         void* args[] = {&qq, &kk, &vv, &out, &C, &P};
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_rowwise_kernel<__bf16>), grid, dim3(512), args, 0,
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_rowwise_kernel<__bf16>), grid, dim3(64 * kRowWaves),
+                            args, 0,
                             stream);
     } else {
         const float *qq = static_cast<const float*>(q), *kk = static_cast<const float*>(kCache),
                     *vv = static_cast<const float*>(vCache);
         void* args[] = {&qq, &kk, &vv, &out, &C, &P};
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_rowwise_kernel<float>), grid, dim3(512), args, 0,
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_rowwise_kernel<float>), grid, dim3(64 * kRowWaves),
+                            args, 0,
                             stream);
     }
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;

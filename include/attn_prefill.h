@@ -128,12 +128,14 @@ attn_status_t attn_prefill_paged(const void* q, const void* kPages, const void* 
                                  hipStream_t stream);
 
 /*
- * attn_prefill_rowwise -- the same result as attn_prefill, computed by the
- * per-row algorithm of the starter kernel in "Inference Attention 2" (Starter
- * code): no tiling, one (row, head) per 32 lanes, the online softmax updated
- * key by key, every row re-reading its whole K/V prefix.  A baseline to time
- * the tiled kernel against (the page's SPEEDUP), not a fast path.  Same
- * arguments, layout, ownership and return codes as attn_prefill.
+ * attn_prefill_rowwise -- the same result as attn_prefill with no tiling
+ * ("Inference Attention 2", Lesson: the starter serves each (row, head) on its
+ * own and every row streams its whole K/V prefix from memory).  One 64-lane
+ * wave per (row, head), keys in blocks of 64: scores with one lane per key,
+ * the weighted sum of V with one lane per dim, one online softmax update per
+ * block.  A baseline to time the tiled kernel against (the page's SPEEDUP),
+ * not a fast path.  Same arguments, layout, ownership and return codes as
+ * attn_prefill.
  */
 attn_status_t attn_prefill_rowwise(const void* q, const void* kCache, const void* vCache, float* out,
                                    int C, int P, attn_dtype_t dtype, hipStream_t stream);

@@ -73,3 +73,25 @@ def test_naive_agrees_with_fused():
     a = cpf.attn_naive(g(q), g(k), g(v)).cpu().numpy()
     b = cpf.attn_prefill(g(q), g(k), g(v), P=0).cpu().numpy()
     assert np.allclose(a, b, rtol=1e-4, atol=1e-5)
+
+
+def test_side_stream_without_context_keeps_its_allocations_on_that_stream():
+    """The score-matrix workspace and out that the binding allocates for a
+    call on an explicit side stream (outside any stream context) belong to
+    that stream (see the split-KV test of the same name)."""
+    T = 300
+    q, k, v, _ = synth.case_planted_chunk(T, 0, 6400, 3)
+    qd, kd, vd = g(q), g(k), g(v)
+    need = cpf.naive_workspace(T)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(20_000_000)
+    out = cpf.attn_naive(qd, kd, vd, stream=s)
+    junk = torch.full((need // 4 + 64,), float("nan"), device=dev())
+    snap = torch.cuda.memory_snapshot()
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert s.cuda_stream in {seg["stream"] for seg in snap if seg.get("total_size", 0) >= need}
+    check(out.cpu().numpy(), oracle.attn_prefill(q, k, v, 0), "naive on a side stream")
+    del junk

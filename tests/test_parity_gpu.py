@@ -155,6 +155,28 @@ def test_cfg5_bf16_c4096_p28672_sampled():
     check_close(got[rr, hh], ref, "bf16", "bf16 C=4096 P=28672 sampled", absref)
 
 
+@pytest.mark.timeout(900)
+def test_cfg5_bf16_c4096_p28672_every_element():
+    """Every one of the 8,388,608 outputs against the oracle on the
+    bf16-rounded inputs, under the stated bound 1e-5 + 2^-8 A (A the oracle on
+    |V|).  The error statistics are printed, with the largest error as a
+    fraction of the stated bound and of the looser 1e-3 + 1e-2 |ref|."""
+    C, P = 4096, 28672
+    q, k, v = synth.case_plain(C, P, 500)
+    got = run_gpu(q, k, v, P, "bf16")
+    qo, ko, vo = oracle_inputs(q, "bf16"), oracle_inputs(k, "bf16"), oracle_inputs(v, "bf16")
+    ref = oracle.attn_prefill(qo, ko, vo, P)
+    absref = oracle.attn_prefill(qo, ko, np.abs(vo), P)
+    check_close(got, ref, "bf16", "bf16 C=4096 P=28672 every element", absref)
+    g, r, a = got.astype(np.float64), ref.astype(np.float64), absref.astype(np.float64)
+    err = np.abs(g - r)
+    big = np.abs(r) >= 1e-3
+    print("\nbf16 C=4096 P=28672, %d elements: max abs err %.3g, max rel err %.3g (|ref| >= 1e-3), RMS %.3g; "
+          "largest error / (1e-5 + 2^-8 A) %.4f, / (1e-3 + 1e-2 |ref|) %.4f"
+          % (err.size, err.max(), (err[big] / np.abs(r[big])).max(), np.sqrt(np.mean(err ** 2)),
+             (err / (BF16_ABS + BF16_REL_OF_A * a)).max(), (err / (1e-3 + 1e-2 * np.abs(r))).max()))
+
+
 # --- the page's edge grid and launch-plan coverage ----------------------------
 
 @pytest.mark.parametrize("C", [1, 17, 33])

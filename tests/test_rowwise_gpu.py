@@ -1,6 +1,7 @@
-"""GPU parity of the per-row baseline (the starter algorithm of "Inference
-Attention 2", Starter code) against the oracle; tolerances as in
-test_parity_gpu.py."""
+"""GPU parity of the per-row baseline (no tiling, every row streams its whole
+K/V prefix, as the starter of "Inference Attention 2" does; Lesson) against
+the oracle; tolerances as in test_parity_gpu.py.  Shapes cover partial and
+several 64-key blocks, rows of one key and the bf16 path."""
 import numpy as np
 import pytest
 import torch

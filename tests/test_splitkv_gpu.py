@@ -128,3 +128,29 @@ def test_decode_deterministic():
     a, _ = run(q, k, v, 9999)
     b, _ = run(q, k, v, 9999)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_side_stream_without_context_keeps_its_allocations_on_that_stream():
+    """A call on an explicit side stream, made outside any stream context,
+    with out and workspace allocated by the binding: both must be allocated on
+    the side stream, so torch's caching allocator does not hand the freed
+    workspace to the current stream while the side stream's kernels may still
+    use it.  The side stream is held back by a spin first, so the kernels run
+    after the binding has returned and freed the workspace."""
+    C, P = 17, 3000
+    q, k, v, plants = synth.case_planted_chunk(C, P, 7400, 3)
+    qd, kd, vd = gpu(q), gpu(k), gpu(v)
+    need, _ = cpf.splitkv_workspace(C, P, torch.float32)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(20_000_000)
+    out = cpf.attn_prefill_splitkv(qd, kd, vd, P=P, stream=s)
+    junk = torch.full((need // 4 + 64,), float("nan"), device="cuda")   # current stream, runs at once
+    snap = torch.cuda.memory_snapshot()
+    s.synchronize()
+    torch.cuda.synchronize()
+    streams = {seg["stream"] for seg in snap if seg.get("total_size", 0) >= need}
+    assert s.cuda_stream in streams
+    close_f32(out.cpu().numpy(), oracle.attn_prefill(q, k, v, P))
+    del junk
