@@ -21,7 +21,7 @@ import os
 import torch  # imported first so the library binds to torch's HIP runtime
 
 __all__ = ["attn_prefill", "attn_prefill_paged", "attn_prefill_rowwise", "attn_prefill_splitkv",
-           "splitkv_workspace", "attn_naive", "naive_workspace", "validate", "paged_validate", "plan",
+           "attn_prefill_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES", "splitkv_workspace", "attn_naive", "naive_workspace", "validate", "paged_validate", "plan",
            "status_string", "library_path", "load_library", "flops", "visible_pairs", "AttnError",
            "EXPORTED_SYMBOLS", "HQ", "HKV", "D"]
 
@@ -34,11 +34,15 @@ _lib = None
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_status_string", "attn_prefill_validate", "attn_prefill_plan",
                     "attn_prefill_version", "attn_prefill_paged", "attn_prefill_paged_validate",
                     "attn_prefill_rowwise", "attn_prefill_splitkv", "attn_prefill_splitkv_workspace",
-                    "attn_naive", "attn_naive_workspace")
+                    "attn_naive", "attn_naive_workspace", "attn_prefill_splitkv_noalloc")
+
+# ATTN_NOALLOC_SCRATCH_BYTES of include/attn_prefill.h
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_NULL_PTR", 3: "ATTN_ERR_UNSUPPORTED_DTYPE",
-          4: "ATTN_ERR_MISALIGNED", 5: "ATTN_ERR_LAUNCH", 6: "ATTN_ERR_ALIAS", 7: "ATTN_ERR_WORKSPACE"}
+          4: "ATTN_ERR_MISALIGNED", 5: "ATTN_ERR_LAUNCH", 6: "ATTN_ERR_ALIAS", 7: "ATTN_ERR_WORKSPACE",
+          8: "ATTN_ERR_TOO_LARGE"}
 
 
 class AttnError(RuntimeError):
@@ -69,6 +73,8 @@ def load_library():
     lib.attn_prefill.restype = i
     lib.attn_prefill_splitkv.argtypes = [vp, vp, vp, vp, i, i, i, vp, ctypes.c_size_t, vp]
     lib.attn_prefill_splitkv.restype = i
+    lib.attn_prefill_splitkv_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, vp]
+    lib.attn_prefill_splitkv_noalloc.restype = i
     lib.attn_prefill_splitkv_workspace.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int)]
     lib.attn_prefill_splitkv_workspace.restype = i
     lib.attn_naive.argtypes = [vp, vp, vp, vp, i, vp, ctypes.c_size_t, vp]
@@ -277,6 +283,35 @@ def attn_prefill_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out:
                                       workspace.data_ptr(), nbytes, s.cuda_stream)
     if st != 0:
         raise AttnError(st, "attn_prefill_splitkv")
+    return out
+
+
+def attn_prefill_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                                 P: int | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """attn_prefill_splitkv with the key-split partials in the library's fixed
+    per-device scratch array (NOALLOC_SCRATCH_BYTES) instead of a workspace:
+    neither this call nor the library allocates anything, so `out` must be
+    given.  Calls on one device share the array and must be ordered on one
+    stream.  Raises AttnError (ATTN_ERR_TOO_LARGE) when the call's partials do
+    not fit the array."""
+    if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype in %s" % list(DTYPES))
+    if out is None:
+        raise ValueError("attn_prefill_splitkv_noalloc allocates nothing: pass out")
+    C = q.shape[0]
+    if P is None:
+        P = k.shape[0] - C
+    if q.dim() != 3 or q.shape[1:] != (HQ, D) or k.shape != (P + C, HKV, D) or v.shape != k.shape:
+        raise ValueError("bad shapes q %s k %s v %s for P=%d" % (tuple(q.shape), tuple(k.shape), tuple(v.shape), P))
+    _gpu_tensors(q.device, q=q, k=k, v=v)
+    s = _stream(stream, q.device)
+    out = _out_tensor(out, C, q.device, s)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_prefill_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), C, P,
+                                              DTYPES[q.dtype], s.cuda_stream)
+    if st != 0:
+        raise AttnError(st, "attn_prefill_splitkv_noalloc")
     return out
 
 

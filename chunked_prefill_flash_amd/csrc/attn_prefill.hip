@@ -60,9 +60,18 @@
 #include <stdint.h>
 #include <limits.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "attn_prefill.h"
+
+// Fixed device scratch for attn_prefill_splitkv_noalloc (callers that cannot
+// allocate): the key-split partials live here instead of in a caller
+// workspace.  Each device the library runs on holds its own copy for the life
+// of the process.  Host code never passes this name to a kernel (on the host
+// it is only a stand-in for the symbol); it passes the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -1326,6 +1335,50 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+attn_status_t scratch_address(void** addr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_ERR_LAUNCH;
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return ATTN_OK;
+}
+
+// The two kernels of a split-KV call: split partials into `part`, then merge
+// them into `out`.  Arguments are already checked.
+attn_status_t launch_splitkv(const Plan& p, const void* q, const void* kCache, const void* vCache, float* out,
+                             int C, int P, attn_dtype_t dtype, float* part, hipStream_t stream) {
+    const PagedCache none{nullptr, 1, 0};
+    const KeySplit ksp{part, p.split_len, p.splits};
+    int len = p.split_len, n = p.splits;
+    hipError_t e;
+    if (p.variant == kV_decode) {
+        void* dargs[] = {const_cast<void**>(&q), const_cast<void**>(&kCache), const_cast<void**>(&vCache), &part, &P,
+                         &len, &n};
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_decode_split_kernel), dim3(p.grid), dim3(p.threads),
+                            dargs, 0, stream);
+    } else {
+        e = dtype == ATTN_DTYPE_BF16 ? dispatch<__bf16, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream)
+                                     : dispatch<float, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream);
+    }
+    if (e != hipSuccess) return ATTN_ERR_LAUNCH;
+    const float* pc = part;
+    void* args[] = {&pc, &out, &C, &P, &len, &n};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_merge_splits_kernel), dim3((C * kHQ + 3) / 4),
+                        dim3(256), args, 0, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1407,26 +1460,19 @@ attn_status_t attn_prefill_splitkv(const void* q, const void* kCache, const void
     if (overlaps(workspace, need, q, nq * esz) || overlaps(workspace, need, kCache, nkv * esz) ||
         overlaps(workspace, need, vCache, nkv * esz) || overlaps(workspace, need, out, nq * 4))
         return ATTN_ERR_ALIAS;
-    const PagedCache none{nullptr, 1, 0};
-    const KeySplit ksp{static_cast<float*>(workspace), p.split_len, p.splits};
-    int len = p.split_len, n = p.splits;
-    hipError_t e;
-    if (p.variant == kV_decode) {
-        float* wsp = static_cast<float*>(workspace);
-        void* dargs[] = {const_cast<void**>(&q), const_cast<void**>(&kCache), const_cast<void**>(&vCache), &wsp, &P,
-                         &len, &n};
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_decode_split_kernel), dim3(p.grid), dim3(p.threads),
-                            dargs, 0, stream);
-    } else {
-        e = dtype == ATTN_DTYPE_BF16 ? dispatch<__bf16, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream)
-                                     : dispatch<float, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream);
-    }
-    if (e != hipSuccess) return ATTN_ERR_LAUNCH;
-    const float* part = static_cast<const float*>(workspace);
-    void* args[] = {&part, &out, &C, &P, &len, &n};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_merge_splits_kernel), dim3((C * kHQ + 3) / 4),
-                        dim3(256), args, 0, stream);
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    return launch_splitkv(p, q, kCache, vCache, out, C, P, dtype, static_cast<float*>(workspace), stream);
+}
+
+attn_status_t attn_prefill_splitkv_noalloc(const void* q, const void* kCache, const void* vCache, float* out,
+                                           int C, int P, attn_dtype_t dtype, hipStream_t stream) {
+    const attn_status_t st = attn_prefill_validate(q, kCache, vCache, out, C, P, dtype);
+    if (st != ATTN_OK || C == 0) return st;
+    const Plan p = split_plan(C, P, dtype);
+    if (split_workspace_bytes(p, C) > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    const attn_status_t sa = scratch_address(&ws);
+    if (sa != ATTN_OK) return sa;
+    return launch_splitkv(p, q, kCache, vCache, out, C, P, dtype, static_cast<float*>(ws), stream);
 }
 
 attn_status_t attn_naive_workspace(int T, size_t* bytes) {
@@ -1544,6 +1590,7 @@ const char* attn_status_string(attn_status_t s) {
         case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH";
         case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS";
         case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+        case ATTN_ERR_TOO_LARGE: return "ATTN_ERR_TOO_LARGE";
     }
     return "ATTN_ERR_UNKNOWN";
 }

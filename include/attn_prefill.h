@@ -26,9 +26,10 @@
  *     out    [C][32][64]      float32 for every dtype
  *
  * Ownership: every pointer is device memory owned by the caller.  The library
- * allocates nothing, keeps no state between calls, and may be called from any
- * host thread.  Work is enqueued on `stream` and the call returns without
- * waiting; the caller synchronises.  `out` must not overlap the inputs; every
+ * allocates nothing and may be called from any host thread.  It keeps no state
+ * between calls, except that attn_prefill_splitkv_noalloc uses one fixed
+ * scratch array per device (see there).  Work is enqueued on `stream` and the
+ * call returns without waiting; the caller synchronises.  `out` must not overlap the inputs; every
  * element of out[0..C) is overwritten.
  *
  * Every entry point only enqueues kernels on `stream`: it allocates,
@@ -68,7 +69,8 @@ typedef enum {
     ATTN_ERR_MISALIGNED = 4,       /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_LAUNCH = 5,           /* the HIP runtime rejected the launch */
     ATTN_ERR_ALIAS = 6,            /* out (or a workspace) overlaps another argument */
-    ATTN_ERR_WORKSPACE = 7         /* workspace smaller than attn_prefill_splitkv_workspace() */
+    ATTN_ERR_WORKSPACE = 7,        /* workspace smaller than attn_prefill_splitkv_workspace() */
+    ATTN_ERR_TOO_LARGE = 8         /* the call needs more than ATTN_NOALLOC_SCRATCH_BYTES of scratch */
 } attn_status_t;
 
 /*
@@ -165,6 +167,36 @@ attn_status_t attn_prefill_rowwise(const void* q, const void* kCache, const void
 attn_status_t attn_prefill_splitkv(const void* q, const void* kCache, const void* vCache, float* out,
                                    int C, int P, attn_dtype_t dtype, void* workspace, size_t workspaceBytes,
                                    hipStream_t stream);
+
+/* Size of the per-device scratch array behind attn_prefill_splitkv_noalloc. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * attn_prefill_splitkv_noalloc -- attn_prefill_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and result, with the
+ * key-split partials in a fixed scratch array of ATTN_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each device it runs on until the process ends,
+ * instead of a caller workspace.  The call allocates nothing and calls no
+ * allocating routine.
+ *
+ *   q, kCache, vCache, out, C, P, dtype, stream as for attn_prefill; the
+ *   current device must be the device of the tensors and of `stream`.
+ *
+ * All calls on one device share that device's array and leave it holding the
+ * last call's partials; nothing in it needs to start at any value.  Calls
+ * whose kernels can overlap on one device race on the array: order them on
+ * one stream (or otherwise serialise them).  The first call on a device looks
+ * up the array's device address (hipGetSymbolAddress) once.
+ *
+ * Returns as attn_prefill_splitkv; ATTN_ERR_TOO_LARGE, with nothing enqueued,
+ * when attn_prefill_splitkv_workspace() for (C, P, dtype) exceeds
+ * ATTN_NOALLOC_SCRATCH_BYTES (for example C above about 1980 rows); use
+ * attn_prefill or attn_prefill_splitkv there.  ATTN_ERR_LAUNCH also when the
+ * array's address cannot be obtained.
+ */
+attn_status_t attn_prefill_splitkv_noalloc(const void* q, const void* kCache, const void* vCache, float* out,
+                                           int C, int P, attn_dtype_t dtype, hipStream_t stream);
 
 /*
  * attn_prefill_splitkv_workspace -- bytes of workspace attn_prefill_splitkv

@@ -182,6 +182,22 @@ def test_splitkv_workspace_sizes():
         cpf.splitkv_workspace(-1, 0)
 
 
+def test_noalloc_rejects_before_any_device_call(lib):
+    """Argument errors and calls whose partials exceed the fixed scratch array
+    return before any HIP call (fake pointers, never dereferenced)."""
+    TOO_LARGE = 8
+    f = lib.attn_prefill_splitkv_noalloc
+    assert f(A, A + 64 * MB, A + 128 * MB, A + 192 * MB, -1, 0, F32, None) == INVALID
+    assert f(None, A + 64 * MB, A + 128 * MB, A + 192 * MB, 4, 10, F32, None) == NULLP
+    assert f(A, A + 64 * MB, A + 128 * MB, A + 192 * MB, 4, 10, 7, None) == DTYPE
+    assert f(A, A + 64 * MB, A + 128 * MB, A + 192 * MB, 0, 10, F32, None) == OK      # C == 0: nothing to do
+    for C, P in [(4096, 100), (2048, 0), (1990, 5000)]:
+        need, _ = cpf.splitkv_workspace(C, P)
+        assert need > cpf.NOALLOC_SCRATCH_BYTES
+        assert f(A, A + 64 * MB, A + 128 * MB, A + 256 * MB, C, P, F32, None) == TOO_LARGE
+    assert cpf.status_string(TOO_LARGE) == "ATTN_ERR_TOO_LARGE"
+
+
 def test_splitkv_rejects_small_or_missing_workspace():
     import ctypes
     lib = cpf.load_library()
