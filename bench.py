@@ -54,6 +54,15 @@ WORKLOADS = {
                                "than the 256 MB Infinity Cache holds), split across workgroups"),
     "c1_p32767_bf16_splitkv": (1, 32767, "bf16", 810,
                                "bf16 decode: one token at P=32767 (32768 KV positions), split across workgroups"),
+    "c1_p16383_f32_splitkv_paged16": (1, 16383, "f32", 800,
+                                      "fp32 decode: one token at P=16383 against a cache in shuffled 16-position "
+                                      "pages (block table, 3 spare pages), key range split across workgroups"),
+    "c1_p131071_f32_splitkv_paged16": (1, 131071, "f32", 820,
+                                       "fp32 decode: one token at P=131071 (512 MiB of K/V) against a cache in "
+                                       "shuffled 16-position pages, key range split across workgroups"),
+    "c1_p32767_bf16_splitkv_paged16": (1, 32767, "bf16", 810,
+                                       "bf16 decode: one token at P=32767 against a cache in shuffled 16-position "
+                                       "pages, key range split across workgroups"),
     "c2048_p2048_f32_paged16": (2048, 2048, "f32", 200,
                                 "fp32 C=2048 at P=2048 with the cache in shuffled 16-position pages "
                                 "(block table, 3 spare pages), q/k/v i.i.d. N(0,1)"),
@@ -337,7 +346,9 @@ def main():
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
     def call():
-        if splitkv:
+        if splitkv and paged:
+            cpf.attn_prefill_paged_splitkv(qd, kpd, vpd, tabd, P, out=out, workspace=ws, stream=stream)
+        elif splitkv:
             cpf.attn_prefill_splitkv(qd, kd, vd, out=out, P=P, workspace=ws, stream=stream)
         elif paged:
             cpf.attn_prefill_paged(qd, kpd, vpd, tabd, P, out=out, stream=stream)
@@ -459,13 +470,16 @@ def main():
         result["roofline"]["frac_at_clock"] = round(achieved / (peak * mhz / NOMINAL_MHZ), 4)
     esz = 4 if dt == "f32" else 2
     alg_bytes = C * 32 * 64 * esz + 2 * (P + C) * 8 * 64 * esz + C * 32 * 64 * 4
+    if paged:
+        alg_bytes += -(-(P + C) // page) * 4     # the block table
     if splitkv:
         # decode is bandwidth-bound: roofline against HBM on the compulsory bytes
         gbs = alg_bytes / (kernel_ms * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_entry(name),
                               "kernel": ("attn_decode_split_kernel" if C == 1 and dt == "f32" else
-                                         "attn_prefill_kernel (split)") + " + attn_merge_splits_kernel",
+                                         "attn_prefill_kernel (split)") + (" (paged)" if paged else "") +
+                                        " + attn_merge_splits_kernel",
                               "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": alg_bytes}
     if not args.no_speedup and not paged and not splitkv:
         # the per-row starter algorithm on the same inputs, same run: the page's SPEEDUP

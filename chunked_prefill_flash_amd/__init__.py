@@ -20,7 +20,8 @@ import os
 
 import torch  # imported first so the library binds to torch's HIP runtime
 
-__all__ = ["attn_prefill", "attn_prefill_paged", "attn_prefill_rowwise", "attn_prefill_splitkv",
+__all__ = ["attn_prefill", "attn_prefill_paged", "attn_prefill_paged_splitkv", "attn_prefill_rowwise",
+           "attn_prefill_splitkv",
            "attn_prefill_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES", "splitkv_workspace", "attn_naive", "naive_workspace", "validate", "paged_validate", "plan",
            "status_string", "library_path", "load_library", "flops", "visible_pairs", "AttnError",
            "EXPORTED_SYMBOLS", "HQ", "HKV", "D"]
@@ -34,7 +35,8 @@ _lib = None
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_status_string", "attn_prefill_validate", "attn_prefill_plan",
                     "attn_prefill_version", "attn_prefill_paged", "attn_prefill_paged_validate",
                     "attn_prefill_rowwise", "attn_prefill_splitkv", "attn_prefill_splitkv_workspace",
-                    "attn_naive", "attn_naive_workspace", "attn_prefill_splitkv_noalloc")
+                    "attn_naive", "attn_naive_workspace", "attn_prefill_splitkv_noalloc",
+                    "attn_prefill_paged_splitkv")
 
 # ATTN_NOALLOC_SCRATCH_BYTES of include/attn_prefill.h
 NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -89,6 +91,8 @@ def load_library():
     lib.attn_prefill_plan.restype = i
     lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, i, i, vp, i, i, i, vp]
     lib.attn_prefill_paged.restype = i
+    lib.attn_prefill_paged_splitkv.argtypes = [vp, vp, vp, vp, i, i, vp, i, i, i, vp, ctypes.c_size_t, vp]
+    lib.attn_prefill_paged_splitkv.restype = i
     lib.attn_prefill_paged_validate.argtypes = [vp, vp, vp, vp, i, i, vp, i, i, i]
     lib.attn_prefill_paged_validate.restype = i
     lib.attn_status_string.argtypes = [i]
@@ -214,15 +218,8 @@ def attn_prefill_rowwise(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out:
     return attn_prefill(q, k, v, out=out, P=P, stream=stream, _entry="attn_prefill_rowwise")
 
 
-def attn_prefill_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
-                       P: int, out: torch.Tensor | None = None,
-                       stream: torch.cuda.Stream | None = None) -> torch.Tensor:
-    """Causal GQA attention of q [C][32][64] against a paged cache.
-
-    k_pages, v_pages: [numBlocks][pageSize][8][64], same dtype as q;
-    block_table: int32 with at least ceil((P+C)/pageSize) physical page indices.
-    Cache position t lives at slot t % pageSize of page block_table[t // pageSize].
-    """
+def _paged_args(q, k_pages, v_pages, block_table, P):
+    """Checks of the paged entry points; returns (C, numBlocks, pageSize)."""
     if q.dtype not in DTYPES or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise TypeError("q, k_pages, v_pages must share one dtype in %s" % list(DTYPES))
     if q.dim() != 3 or q.shape[1:] != (HQ, D):
@@ -236,6 +233,19 @@ def attn_prefill_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
             block_table.shape[0] < -(-(P + C) // page_size):
         raise ValueError("block_table must be int32 with at least ceil((P+C)/pageSize) entries")
     _gpu_tensors(q.device, q=q, k_pages=k_pages, v_pages=v_pages, block_table=block_table)
+    return C, num_blocks, page_size
+
+
+def attn_prefill_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                       P: int, out: torch.Tensor | None = None,
+                       stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Causal GQA attention of q [C][32][64] against a paged cache.
+
+    k_pages, v_pages: [numBlocks][pageSize][8][64], same dtype as q;
+    block_table: int32 with at least ceil((P+C)/pageSize) physical page indices.
+    Cache position t lives at slot t % pageSize of page block_table[t // pageSize].
+    """
+    C, num_blocks, page_size = _paged_args(q, k_pages, v_pages, block_table, P)
     s = _stream(stream, q.device)
     out = _out_tensor(out, C, q.device, s)
     lib = load_library()
@@ -244,6 +254,29 @@ def attn_prefill_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Te
                                     num_blocks, page_size, out.data_ptr(), C, P, DTYPES[q.dtype], s.cuda_stream)
     if st != 0:
         raise AttnError(st, "attn_prefill_paged")
+    return out
+
+
+def attn_prefill_paged_splitkv(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                               block_table: torch.Tensor, P: int, out: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None,
+                               stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """attn_prefill_paged with the key range split across workgroups and the
+    partials merged (decode against a paged cache).  Arguments as for
+    attn_prefill_paged; workspace as for attn_prefill_splitkv (at least
+    splitkv_workspace(C, P, dtype)[0] bytes; allocated if None)."""
+    C, num_blocks, page_size = _paged_args(q, k_pages, v_pages, block_table, P)
+    s = _stream(stream, q.device)
+    out = _out_tensor(out, C, q.device, s)
+    workspace = _workspace(workspace, splitkv_workspace(C, P, q.dtype)[0], q.device, s)
+    nbytes = workspace.numel() * workspace.element_size()
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_prefill_paged_splitkv(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                            block_table.data_ptr(), num_blocks, page_size, out.data_ptr(), C, P,
+                                            DTYPES[q.dtype], workspace.data_ptr(), nbytes, s.cuda_stream)
+    if st != 0:
+        raise AttnError(st, "attn_prefill_paged_splitkv")
     return out
 
 

@@ -186,7 +186,8 @@ struct KeySplit {
     int n;          // number of splits
 };
 
-enum Mode { kPlain = 0, kPaged = 1, kSplit = 2 };
+// Kernel modes, as bits: a paged cache, a key-range split, or both.
+enum Mode { kPlain = 0, kPaged = 1, kSplit = 2, kPagedSplit = 3 };
 
 // ---------------------------------------------------------------------------
 // The kernel.  One workgroup = one KV group g and one or two row tiles.
@@ -200,8 +201,8 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     using G = Geo<T, NW, KS>;
     constexpr int kBK = G::kBK, kNB = G::kNB, kRows = G::kRows, kRB = G::kRowBytes;
     constexpr bool kF32 = sizeof(T) == 4;
-    constexpr bool PAGED = MODE == kPaged;
-    constexpr bool SPLIT = MODE == kSplit;
+    constexpr bool PAGED = (MODE & kPaged) != 0;
+    constexpr bool SPLIT = (MODE & kSplit) != 0;
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[G::kLdsBytes];
 
@@ -889,6 +890,38 @@ __device__ __forceinline__ void load_row8(const float* p, float (&x)[8]) {
     }
 }
 
+__device__ __forceinline__ void load_row8(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&x)[8]) {
+    const f4 a = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    const f4 b = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[e] = a[e];
+        x[4 + e] = b[e];
+    }
+}
+
+// n / d for 0 <= n < 2^32 and a divisor d >= 1 fixed for the launch, as one
+// high multiply, a subtract, an add and two shifts (Granlund and Montgomery,
+// "Division by invariant integers using multiplication", 1994, section 4:
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
+// q = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0) with t = mulhi(m, n)).
+struct FastDiv {
+    uint32_t m;
+    int s1, s2;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return FastDiv{(uint32_t)m, l < 1 ? l : 1, l > 1 ? l - 1 : 0};
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+    const uint32_t t = __umulhi(f.m, n);
+    return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
 // sum over the 8 consecutive lanes of a key slot; every lane ends with the
 // same bits (each step adds the same two values in either order)
 __device__ __forceinline__ float slot_sum8(float x) {
@@ -898,9 +931,14 @@ __device__ __forceinline__ float slot_sum8(float x) {
     return x;
 }
 
+// PAGED: kc and vc are the page pools [numBlocks][pageSize][8][64] and a
+// position's row is found through the block table ("FlashAttention and
+// inference kernels", section PagedAttention); the table entries of a chunk's
+// keys are read one chunk ahead, so a row load waits on no table read.
+template <bool PAGED>
 __global__ void __launch_bounds__(64 * kDecWaves)
 attn_decode_split_kernel(const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
-                         float* __restrict__ part, int P, int len, int n) {
+                         float* __restrict__ part, int P, int len, int n, PagedCache pg, FastDiv pdiv) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -928,7 +966,36 @@ attn_decode_split_kernel(const float* __restrict__ q, const float* __restrict__ 
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
 
+    // Paged cache: the pools and the table are read through buffer
+    // descriptors, so a row whose table entry is out of range (given an
+    // offset past the pool) reads as zero keys and values, as in the tiled
+    // kernel; row offsets are 32-bit (the host bounds pool and table sizes).
+    constexpr uint32_t kRowBytes = kD * 4;
+    const uint32_t pool_bytes = PAGED ? (uint32_t)((size_t)pg.num_blocks * pg.page_size * kHKV * kRowBytes) : 0u;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, pool_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vc, (short)0, pool_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rtab = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)pg.table, (short)0, PAGED ? (uint32_t)((total + pg.page_size - 1) / pg.page_size) * 4u : 0u,
+        0x00020000);
+    // byte offset of this lane's 8 dims of position `key` in the pools
+    auto row_offset = [&](int key, int entry) -> uint32_t {
+        const uint32_t blk = fast_div((uint32_t)key, pdiv);
+        const uint32_t in_page = (uint32_t)key - blk * (uint32_t)pg.page_size;
+        return entry >= 0 && entry < pg.num_blocks
+                   ? (((uint32_t)entry * (uint32_t)pg.page_size + in_page) * kHKV + g) * kRowBytes + 32u * ds
+                   : pool_bytes;
+    };
+    auto table_entry = [&](int key) -> int {   // key < kend, or the entry is not used
+        const uint32_t blk = fast_div((uint32_t)min(key, kend - 1), pdiv);
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, blk * 4u, 0, 0);
+    };
+
     constexpr int kStep = 8 * kDecWaves;    // keys between a wave's consecutive chunks
+    int ent[kDecUnroll] = {};               // paged: table entries of this iteration's keys
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) ent[u] = table_entry(kbeg + 8 * w + kStep * u + slot);
+    }
     for (int c0 = kbeg + 8 * w; c0 < kend; c0 += kStep * kDecUnroll) {
         float kx[kDecUnroll][8], vx[kDecUnroll][8];
         bool ok[kDecUnroll];
@@ -936,9 +1003,20 @@ attn_decode_split_kernel(const float* __restrict__ q, const float* __restrict__ 
         for (int u = 0; u < kDecUnroll; ++u) {
             const int key = c0 + kStep * u + slot;
             ok[u] = key < kend;
-            const size_t off = ((size_t)(ok[u] ? key : kbeg) * kHKV + g) * kD + 8 * ds;   // in range either way
-            load_row8(kc + off, kx[u]);
-            load_row8(vc + off, vx[u]);
+            if constexpr (PAGED) {
+                const uint32_t off = row_offset(ok[u] ? key : kbeg, ok[u] ? ent[u] : -1);
+                load_row8(rk, off, kx[u]);
+                load_row8(rv, off, vx[u]);
+            } else {
+                const size_t off = ((size_t)(ok[u] ? key : kbeg) * kHKV + g) * kD + 8 * ds;   // in range either way
+                load_row8(kc + off, kx[u]);
+                load_row8(vc + off, vx[u]);
+            }
+        }
+        if constexpr (PAGED) {
+            // the next iteration's table entries, in flight during this one's math
+#pragma unroll
+            for (int u = 0; u < kDecUnroll; ++u) ent[u] = table_entry(c0 + kStep * kDecUnroll + kStep * u + slot);
         }
 #pragma unroll
         for (int u = 0; u < kDecUnroll; ++u) {
@@ -1265,14 +1343,14 @@ hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, 
                     PagedCache pg, KeySplit ksp, hipStream_t stream) {
     switch (p.variant) {
         case kV_4x2:
-            if constexpr (MODE == kSplit) return hipErrorInvalidValue;   // never planned
+            if constexpr ((MODE & kSplit) != 0) return hipErrorInvalidValue;   // never planned
             else return launch<T, 4, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
         case kV_2x4: return launch<T, 2, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
         case kV_8x2:   // planned for bf16 contiguous caches only
             if constexpr (MODE != kPlain || sizeof(T) != 2) return hipErrorInvalidValue;
             else return launch<T, 8, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
         case kV_4x4:   // planned for fp32 only, never with key splits
-            if constexpr (MODE == kSplit || sizeof(T) != 4) return hipErrorInvalidValue;
+            if constexpr ((MODE & kSplit) != 0 || sizeof(T) != 4) return hipErrorInvalidValue;
             else return launch<T, 4, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
         default: return launch<T, 1, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
     }
@@ -1355,21 +1433,28 @@ attn_status_t scratch_address(void** addr) {
 }
 
 // The two kernels of a split-KV call: split partials into `part`, then merge
-// them into `out`.  Arguments are already checked.
+// them into `out`.  pg.table == nullptr: contiguous cache; otherwise kCache and
+// vCache are page pools read through pg.  Arguments are already checked.
 attn_status_t launch_splitkv(const Plan& p, const void* q, const void* kCache, const void* vCache, float* out,
-                             int C, int P, attn_dtype_t dtype, float* part, hipStream_t stream) {
-    const PagedCache none{nullptr, 1, 0};
+                             int C, int P, attn_dtype_t dtype, float* part, PagedCache pg, hipStream_t stream) {
+    const bool paged = pg.table != nullptr;
     const KeySplit ksp{part, p.split_len, p.splits};
     int len = p.split_len, n = p.splits;
     hipError_t e;
     if (p.variant == kV_decode) {
+        FastDiv pdiv = make_fastdiv((uint32_t)pg.page_size);
         void* dargs[] = {const_cast<void**>(&q), const_cast<void**>(&kCache), const_cast<void**>(&vCache), &part, &P,
-                         &len, &n};
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_decode_split_kernel), dim3(p.grid), dim3(p.threads),
-                            dargs, 0, stream);
+                         &len, &n, &pg, &pdiv};
+        const void* fn = paged ? reinterpret_cast<const void*>(&attn_decode_split_kernel<true>)
+                               : reinterpret_cast<const void*>(&attn_decode_split_kernel<false>);
+        e = hipLaunchKernel(fn, dim3(p.grid), dim3(p.threads), dargs, 0, stream);
+    } else if (paged) {
+        e = dtype == ATTN_DTYPE_BF16
+                ? dispatch<__bf16, kPagedSplit>(p, q, kCache, vCache, out, C, P, pg, ksp, stream)
+                : dispatch<float, kPagedSplit>(p, q, kCache, vCache, out, C, P, pg, ksp, stream);
     } else {
-        e = dtype == ATTN_DTYPE_BF16 ? dispatch<__bf16, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream)
-                                     : dispatch<float, kSplit>(p, q, kCache, vCache, out, C, P, none, ksp, stream);
+        e = dtype == ATTN_DTYPE_BF16 ? dispatch<__bf16, kSplit>(p, q, kCache, vCache, out, C, P, pg, ksp, stream)
+                                     : dispatch<float, kSplit>(p, q, kCache, vCache, out, C, P, pg, ksp, stream);
     }
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
     const float* pc = part;
@@ -1460,7 +1545,8 @@ attn_status_t attn_prefill_splitkv(const void* q, const void* kCache, const void
     if (overlaps(workspace, need, q, nq * esz) || overlaps(workspace, need, kCache, nkv * esz) ||
         overlaps(workspace, need, vCache, nkv * esz) || overlaps(workspace, need, out, nq * 4))
         return ATTN_ERR_ALIAS;
-    return launch_splitkv(p, q, kCache, vCache, out, C, P, dtype, static_cast<float*>(workspace), stream);
+    return launch_splitkv(p, q, kCache, vCache, out, C, P, dtype, static_cast<float*>(workspace),
+                          PagedCache{nullptr, 1, 0}, stream);
 }
 
 attn_status_t attn_prefill_splitkv_noalloc(const void* q, const void* kCache, const void* vCache, float* out,
@@ -1472,7 +1558,8 @@ attn_status_t attn_prefill_splitkv_noalloc(const void* q, const void* kCache, co
     void* ws = nullptr;
     const attn_status_t sa = scratch_address(&ws);
     if (sa != ATTN_OK) return sa;
-    return launch_splitkv(p, q, kCache, vCache, out, C, P, dtype, static_cast<float*>(ws), stream);
+    return launch_splitkv(p, q, kCache, vCache, out, C, P, dtype, static_cast<float*>(ws), PagedCache{nullptr, 1, 0},
+                          stream);
 }
 
 attn_status_t attn_naive_workspace(int T, size_t* bytes) {
@@ -1578,6 +1665,30 @@ attn_status_t attn_prefill_paged(const void* q, const void* kPages, const void* 
                              ? dispatch<__bf16, kPaged>(p, q, kPages, vPages, out, C, P, pg, nosplit, stream)
                              : dispatch<float, kPaged>(p, q, kPages, vPages, out, C, P, pg, nosplit, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_prefill_paged_splitkv(const void* q, const void* kPages, const void* vPages,
+                                         const int* blockTable, int numBlocks, int pageSize, float* out, int C, int P,
+                                         attn_dtype_t dtype, void* workspace, size_t workspaceBytes,
+                                         hipStream_t stream) {
+    const attn_status_t st =
+        attn_prefill_paged_validate(q, kPages, vPages, blockTable, numBlocks, pageSize, out, C, P, dtype);
+    if (st != ATTN_OK || C == 0) return st;
+    const Plan p = split_plan(C, P, dtype);
+    const size_t need = split_workspace_bytes(p, C);
+    if (!workspace) return ATTN_ERR_NULL_PTR;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return ATTN_ERR_MISALIGNED;
+    if (workspaceBytes < need) return ATTN_ERR_WORKSPACE;
+    const size_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
+    const size_t nq = (size_t)C * kHQ * kD;
+    const size_t pool = (size_t)numBlocks * (size_t)pageSize * kHKV * kD * esz;
+    const size_t ntab = ((size_t)P + C + pageSize - 1) / pageSize;
+    if (overlaps(workspace, need, q, nq * esz) || overlaps(workspace, need, kPages, pool) ||
+        overlaps(workspace, need, vPages, pool) || overlaps(workspace, need, blockTable, ntab * 4) ||
+        overlaps(workspace, need, out, nq * 4))
+        return ATTN_ERR_ALIAS;
+    return launch_splitkv(p, q, kPages, vPages, out, C, P, dtype, static_cast<float*>(workspace),
+                          PagedCache{blockTable, pageSize, numBlocks}, stream);
 }
 
 const char* attn_status_string(attn_status_t s) {

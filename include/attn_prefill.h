@@ -206,6 +206,32 @@ attn_status_t attn_prefill_splitkv_noalloc(const void* q, const void* kCache, co
 attn_status_t attn_prefill_splitkv_workspace(int C, int P, attn_dtype_t dtype, size_t* bytes, int* splits);
 
 /*
+ * attn_prefill_paged_splitkv -- attn_prefill_splitkv over a paged cache: the
+ * key range of each row tile split across workgroups, the partials merged
+ * ("FlashAttention and inference kernels", sections "Parallelism during
+ * decode: Flash-Decoding and split-K" and "A paged decode attention kernel
+ * (with GQA)"), with every K/V row found through the block table as in
+ * attn_prefill_paged (section PagedAttention).  The decode shape against a
+ * paged cache: one token (or a short chunk) over a long prefix, where row
+ * tiles x KV groups alone would leave most of the GPU idle.  One fp32 token
+ * runs on the FMA kernel, everything else on the tiled MFMA kernel.
+ *
+ *   q, kPages, vPages, blockTable, numBlocks, pageSize, out, C, P, dtype as
+ *   for attn_prefill_paged; workspace and workspaceBytes as for
+ *   attn_prefill_splitkv, sized by attn_prefill_splitkv_workspace(C, P, dtype)
+ *   (the same plan); stream as for attn_prefill.
+ *
+ * A table entry outside [0, numBlocks) reads as zeros, as in
+ * attn_prefill_paged.  Returns as attn_prefill_paged, and as
+ * attn_prefill_splitkv for the workspace (ATTN_ERR_ALIAS also when it overlaps
+ * the pools or the table).
+ */
+attn_status_t attn_prefill_paged_splitkv(const void* q, const void* kPages, const void* vPages,
+                                         const int* blockTable, int numBlocks, int pageSize, float* out, int C, int P,
+                                         attn_dtype_t dtype, void* workspace, size_t workspaceBytes,
+                                         hipStream_t stream);
+
+/*
  * attn_naive -- causal prompt prefill (P = 0) by the three-kernel pipeline of
  * "Inference Attention 1: The Full Score Matrix" (Lesson): a scores kernel
  * writes the 32 x T x T fp32 score matrix (-inf above the diagonal) into

@@ -147,6 +147,29 @@ def test_paged_validate_codes():
     assert pv(out=A + 64 * MB, kp=A + 64 * MB) == ALIAS
 
 
+def test_paged_splitkv_rejections():
+    """The paged checks of attn_prefill_paged plus the workspace checks of
+    attn_prefill_splitkv, before any device call (fake pointers)."""
+    lib = cpf.load_library()
+    need, _ = cpf.splitkv_workspace(4, 1000)
+    f = lib.attn_prefill_paged_splitkv
+    base = dict(q=A, kp=A + 64 * MB, vp=A + 128 * MB, tab=A + 192 * MB, nb=80, ps=16, out=A + 196 * MB, C=4, P=1000)
+
+    def call(ws, nbytes, **kw):
+        a = dict(base, **kw)
+        return f(a["q"], a["kp"], a["vp"], a["tab"], a["nb"], a["ps"], a["out"], a["C"], a["P"], F32, ws, nbytes,
+                 None)
+    ws = A + 256 * MB
+    assert call(ws, need - 16) == WORKSPACE
+    assert call(None, need) == NULLP
+    assert call(ws + 4, need) == MISAL
+    assert call(A + 64 * MB, need) == ALIAS            # workspace on the K pool
+    assert call(A + 192 * MB, need) == ALIAS           # workspace on the table
+    assert call(ws, need, ps=0) == INVALID             # the paged checks come first
+    assert call(ws, need, tab=None) == NULLP
+    assert call(ws, need, C=0) == OK                   # nothing to do
+
+
 def test_fp32_plans_balance_causal_work():
     """Row-tile height and pairing per shape (see the planner's makespan
     estimate): (rows per item, workgroups, items per workgroup)."""
