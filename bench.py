@@ -179,6 +179,194 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
+# ---- rocprofv3 harness ------------------------------------------------------
+# The profiles under profiles/ come from these rocprofv3 passes over this
+# benchmark (one counter set per run: the hardware cannot collect more at
+# once) and from summarize_rocprof() below, which turns their CSV output into
+# the summaries and the traffic table.  Neither function touches the GPU.
+SQ_SET_1 = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS "
+            "SQ_LDS_BANK_CONFLICT SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE")
+SQ_SET_2 = "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_ACTIVE_INST_VALU SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE"
+COPY_MIB = 512   # calibration copy: a plain elementwise op that reads and writes this many MiB
+
+
+def rocprof_passes(name, outdir):
+    """(pass, command) for each rocprofv3 run of workload `name`, writing
+    under outdir/<pass>/."""
+    bench = os.path.join(ROOT, "bench.py")
+    short = ("python %s --workload %s --steps 3 --warmup 1 --warmup-seconds 0 --no-cpu --no-check --no-speedup "
+             "--no-clock --calibrate-copy-mib %d" % (bench, name, COPY_MIB))
+    passes = [("trace", "timeout -s KILL 300 rocprofv3 --kernel-trace --stats",
+               "python %s --workload %s --steps 200 --warmup 20 --no-cpu" % (bench, name)),
+              ("fetch", "timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE", short),
+              ("write", "timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE", short),
+              ("sq1", "timeout -s KILL 90 rocprofv3 --pmc " + SQ_SET_1, short),
+              ("sq2", "timeout -s KILL 90 rocprofv3 --pmc " + SQ_SET_2, short)]
+    return [(p, "cd /tmp && TMPDIR=/tmp %s --output-format csv -d %s -o %s -- %s"
+             % (prof, os.path.join(outdir, p), p, prog)) for p, prof, prog in passes]
+
+
+PRODUCT_KERNELS = ("attn_prefill_kernel", "attn_decode_split_kernel", "attn_merge_splits_kernel")
+
+
+def _short_kernel(name):
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    for k in PRODUCT_KERNELS + ("attn_rowwise_kernel", "naive_scores_kernel", "naive_softmax_kernel",
+                                "naive_pv_kernel"):
+        if n.startswith(k):
+            tmpl = n[len(k):].split("(")[0]
+            return k + tmpl
+    return n.split("(")[0][:70]
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _counters(dirpath):
+    """{counter: {"product": mean per call over the product kernels (summed
+    over the kernels of one call), "copy": mean over the calibration copies,
+    "us": mean profiled duration per call}} from one --pmc pass."""
+    import glob
+    files = glob.glob(os.path.join(dirpath, "*counter_collection.csv"))
+    if not files:
+        return None
+    rows = _read_csv(files[0])
+    per = {}   # counter -> kernel -> list of values
+    dur = {}
+    for r in rows:
+        k = _short_kernel(r["Kernel_Name"])
+        per.setdefault(r["Counter_Name"], {}).setdefault(k, []).append(float(r["Counter_Value"]))
+        dur.setdefault(k, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    out = {}
+    for cname, bykernel in per.items():
+        prod = [k for k in bykernel if k.split("<")[0] in PRODUCT_KERNELS]
+        value = sum(sum(bykernel[k]) / len(bykernel[k]) for k in prod)
+        copies = [v for k, vs in bykernel.items() if "elementwise" in k for v in vs]
+        big = [v for v in copies if copies and v >= 0.9 * max(copies)]
+        out[cname] = {"product": value, "copy": sum(big) / len(big) if big else None,
+                      "kernels": sorted(prod),
+                      "us": sum(sum(dur[k].values()) / len(dur[k]) for k in prod)}
+    return out
+
+
+def summarize_rocprof(name, outdir, profiles_dir=None):
+    """Write <kernel>_<workload>_kernel_trace.md and _counters.md under
+    profiles_dir (default profiles/) from the passes of
+    rocprof_passes(name, outdir) that are present, and record the scaled HBM
+    bytes per call in its traffic.json."""
+    profiles_dir = profiles_dir or os.path.join(ROOT, "profiles")
+    traffic_file = os.path.join(profiles_dir, "traffic.json")
+    import chunked_prefill_flash_amd as cpf
+    C, P, dt, _, desc = WORKLOADS[name]
+    decode = "splitkv" in name
+    base = "attn_decode" if decode and C == 1 else "attn_prefill"
+    src = kernel_source_hash()
+    flop = cpf.flops(C, P)
+    esz = 4 if dt == "f32" else 2
+    alg = C * 32 * 64 * esz + 2 * (P + C) * 8 * 64 * esz + C * 32 * 64 * 4
+    if "paged" in name:
+        alg += -(-(P + C) // int(name.rsplit("paged", 1)[1])) * 4
+    cmds = dict(rocprof_passes(name, outdir))
+    written = []
+    tdir = os.path.join(outdir, "trace")
+    stats = os.path.join(tdir, "trace_kernel_stats.csv")
+    if os.path.exists(stats):
+        rows = _read_csv(stats)
+        md = ["# %s kernel trace: %s" % (base, desc), "",
+              "Kernel source sha256[:16]: `%s`. Command:" % src, "", "```", cmds["trace"], "```", "",
+              "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Std dev (us) | Share |",
+              "|---|---|---|---|---|---|---|"]
+        per_call = 0.0
+        for r in rows:
+            k = _short_kernel(r["Name"])
+            md.append("| %s | %s | %.2f | %.2f | %.2f | %.2f | %s%% |" % (
+                k, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                float(r["StdDev"]) / 1e3, r["Percentage"]))
+            if k.split("<")[0] in PRODUCT_KERNELS:
+                per_call += float(r["AverageNs"]) / 1e3
+        md.append("")
+        if decode:
+            md.append("Per call (the product kernels' averages summed): %.2f us -> %.1f GB/s over %d algorithmic "
+                      "bytes (%.1f%% of 8 TB/s)." % (per_call, alg / per_call / 1e3, alg,
+                                                     alg / per_call / 1e3 / HBM_PEAK_GBS * 100))
+        else:
+            md.append("Per call: %.2f us -> %.1f TFLOP/s over %.4e FLOP (%.1f%% of the %s MFMA peak %.1f TFLOP/s)."
+                      % (per_call, flop / per_call / 1e6, flop, flop / per_call / 1e6 / PEAK_TFLOPS[dt] * 100, dt,
+                         PEAK_TFLOPS[dt]))
+        md.append("")
+        path = os.path.join(profiles_dir, "%s_%s_kernel_trace.md" % (base, name))
+        open(path, "w").write("\n".join(md))
+        written.append(path)
+    cnt = {}
+    for p in ("fetch", "write", "sq1", "sq2"):
+        c = _counters(os.path.join(outdir, p))
+        if c:
+            cnt.update(c)
+    if cnt:
+        copy_bytes = COPY_MIB << 20
+        md = ["# %s counters: %s" % (base, desc), "",
+              "Kernel source sha256[:16]: `%s`. Values are per call (the product kernels of one call summed), "
+              "averaged over the profiled calls." % src, "", "Commands (one counter set per run):", "", "```"]
+        md += [cmds[p] for p in ("fetch", "write", "sq1", "sq2")]
+        md += ["```", "", "The calibration kernel is the benchmark's `--calibrate-copy-mib %d` leg: an elementwise "
+               "`torch.mul(src, 1.0, out=dst)` over %d MiB of float32, which reads and writes %d KiB."
+               % (COPY_MIB, COPY_MIB, copy_bytes >> 10), "", "| Counter | Value |", "|---|---|"]
+        entry = None
+        if "FETCH_SIZE" in cnt and "WRITE_SIZE" in cnt and cnt["FETCH_SIZE"]["copy"] and cnt["WRITE_SIZE"]["copy"]:
+            f, w = cnt["FETCH_SIZE"], cnt["WRITE_SIZE"]
+            fs, ws = copy_bytes / 1024 / f["copy"], copy_bytes / 1024 / w["copy"]
+            hbm = f["product"] * 1024 * fs + w["product"] * 1024 * ws
+            md += ["| kernels | %s |" % ", ".join(f["kernels"]),
+                   "| FETCH_SIZE (KiB per call, raw) | %.1f |" % f["product"],
+                   "| WRITE_SIZE (KiB per call, raw) | %.1f |" % w["product"],
+                   "| copy FETCH_SIZE (KiB) | %.1f -> fetch scale %.4f |" % (f["copy"], fs),
+                   "| copy WRITE_SIZE (KiB) | %.1f -> write scale %.4f |" % (w["copy"], ws),
+                   "| HBM-side bytes per call (scaled) | %.2f MiB (algorithmic %.2f MiB, ratio %.3f) |"
+                   % (hbm / 2 ** 20, alg / 2 ** 20, hbm / alg)]
+            entry = {"kernel_source_sha256_16": src, "bytes_per_launch": int(round(hbm)), "kernels": f["kernels"],
+                     "fetch_kib_raw": round(f["product"], 1), "write_kib_raw": round(w["product"], 1),
+                     "fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "algorithmic_bytes": alg}
+        mops = cnt.get("SQ_INSTS_VALU_MFMA_MOPS_F32" if dt == "f32" else "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        if mops:
+            md.append("| MFMA FLOP (SQ_INSTS_VALU_MFMA_MOPS x 512) | %.4e (algorithmic %.4e) |"
+                      % (mops["product"] * 512, flop))
+        busy = cnt.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        if busy and busy["us"] > 0:
+            per_simd = busy["product"] / 1024
+            cyc = busy["us"] * 1e-6 * NOMINAL_MHZ * 1e6
+            md.append("| SQ_VALU_MFMA_BUSY_CYCLES | %.4e (per SIMD %.4e = %.1f%% of %.0f cycles at 2.4 GHz over "
+                      "the profiled %.1f us) |" % (busy["product"], per_simd, per_simd / cyc * 100, cyc, busy["us"]))
+        for cname in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS",
+                      "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_BUSY_CYCLES",
+                      "GRBM_GUI_ACTIVE", "SQ_WAVES"):
+            if cname in cnt:
+                md.append("| %s | %.4e |" % (cname, cnt[cname]["product"]))
+        if "SQ_INSTS_MFMA" in cnt and "SQ_INSTS_VALU" in cnt and cnt["SQ_INSTS_MFMA"]["product"] > 0:
+            mf, va = cnt["SQ_INSTS_MFMA"]["product"], cnt["SQ_INSTS_VALU"]["product"]
+            md.append("| non-MFMA VALU instructions per MFMA | %.2f |" % ((va - mf) / mf))
+        if "SQ_INSTS_LDS" in cnt and "SQ_LDS_BANK_CONFLICT" in cnt and cnt["SQ_INSTS_LDS"]["product"] > 0:
+            md.append("| LDS bank-conflict cycles per LDS instruction | %.3f |"
+                      % (cnt["SQ_LDS_BANK_CONFLICT"]["product"] / cnt["SQ_INSTS_LDS"]["product"]))
+        md.append("")
+        path = os.path.join(profiles_dir, "%s_%s_counters.md" % (base, name))
+        open(path, "w").write("\n".join(md))
+        written.append(path)
+        if entry:
+            try:
+                table = json.load(open(traffic_file))
+            except (OSError, ValueError):
+                table = {}
+            table[name] = entry
+            with open(traffic_file, "w") as fh:
+                json.dump(table, fh, indent=1, sort_keys=True)
+                fh.write("\n")
+            written.append(traffic_file)
+    return written
+
+
 def make_inputs(name):
     import synth
     C, P, dt, seed, _ = WORKLOADS[name]
@@ -307,11 +495,24 @@ def main():
                     help="also time 20 calls each preceded by a 1 GiB read, so inputs come from HBM "
                          "rather than the 256 MB Infinity Cache")
     ap.add_argument("--no-clock", action="store_true", help="do not sample the shader clock")
+    ap.add_argument("--rocprof-commands", metavar="DIR",
+                    help="print the rocprofv3 passes for --workload (output under DIR/<pass>) and exit")
+    ap.add_argument("--rocprof-summary", metavar="DIR",
+                    help="write the profiles/ summaries and traffic entry for --workload from the rocprofv3 "
+                         "output under DIR/<pass> and exit (no GPU use)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run a plain elementwise copy of this many MiB three times "
                          "(reference kernel of known traffic for HBM byte counters)")
     args = ap.parse_args()
 
+    if args.rocprof_commands:
+        for _, cmd in rocprof_passes(args.workload, os.path.abspath(args.rocprof_commands)):
+            print(cmd)
+        return
+    if args.rocprof_summary:
+        for path in summarize_rocprof(args.workload, os.path.abspath(args.rocprof_summary)):
+            print(path)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)

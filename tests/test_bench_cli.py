@@ -23,3 +23,49 @@ def test_help_lists_the_workloads():
     for w in ("c2048_p2048_f32", "c4096_p28672_bf16", "c1_p16383_f32_splitkv", "c1_p131071_f32_splitkv",
               "c2048_p2048_f32_paged16"):
         assert w in r.stdout
+
+
+def _write_counter_csv(path, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    cols = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+            "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        for i, (kernel, counter, value, dur_ns) in enumerate(rows):
+            w.writerow({"Correlation_Id": i, "Dispatch_Id": i, "Kernel_Name": kernel, "Counter_Name": counter,
+                        "Counter_Value": value, "Start_Timestamp": 1000, "End_Timestamp": 1000 + dur_ns})
+
+
+def test_rocprof_summary_scales_traffic_by_the_copy_calibration(tmp_path):
+    """The harness's CSV -> summary step on synthetic rocprofv3 output: two
+    calls of the prefill kernel, a copy kernel whose FETCH_SIZE reads half
+    its known 512 MiB, so the kernel's fetched KiB are doubled, written KiB
+    taken as they are."""
+    sys.path.insert(0, ROOT)
+    import bench
+    prof = tmp_path / "prof"
+    kern = ("void (anonymous namespace)::attn_prefill_kernel<float, 4, 4, 0>(float const*, float const*, "
+            "float const*, float*, int, int, int, int, (anonymous namespace)::PagedCache, "
+            "(anonymous namespace)::KeySplit)")
+    copy = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>>(int, ...)"
+    half = (512 << 20) // 1024 // 2
+    _write_counter_csv(str(prof / "fetch" / "fetch_counter_collection.csv"),
+                       [(kern, "FETCH_SIZE", 8000.0, 400000), (kern, "FETCH_SIZE", 8400.0, 400000),
+                        (copy, "FETCH_SIZE", half, 90000), (copy, "FETCH_SIZE", 12.0, 1000)])
+    _write_counter_csv(str(prof / "write" / "write_counter_collection.csv"),
+                       [(kern, "WRITE_SIZE", 16384.0, 400000), (kern, "WRITE_SIZE", 16384.0, 400000),
+                        (copy, "WRITE_SIZE", 2 * half, 90000)])
+    out = tmp_path / "profiles"
+    out.mkdir()
+    written = bench.summarize_rocprof("c2048_p2048_f32", str(prof), profiles_dir=str(out))
+    assert len(written) == 2
+    import json
+    e = json.load(open(out / "traffic.json"))["c2048_p2048_f32"]
+    assert e["fetch_scale"] == 2.0 and e["write_scale"] == 1.0
+    assert e["bytes_per_launch"] == int(8200.0 * 1024 * 2 + 16384.0 * 1024)
+    assert e["algorithmic_bytes"] == 48 << 20
+    assert e["kernel_source_sha256_16"] == bench.kernel_source_hash()
+    text = open(out / "attn_prefill_c2048_p2048_f32_counters.md").read()
+    assert "rocprofv3 --pmc FETCH_SIZE" in text and "ratio" in text
