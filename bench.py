@@ -22,7 +22,6 @@ import hashlib
 import json
 import os
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -76,103 +75,20 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 NOMINAL_MHZ = 2400.0   # the clock the published peaks assume
 
 
-class ClockSampler:
-    """Samples the shader (gfx) clock in a background thread while the timed
-    region runs: the per-XCD current_gfxclks of the SMU metrics table, read
-    in-process through the amdsmi library (no subprocess), every `period_s`.
-    Each sample is the mean over the XCDs.  If amdsmi is missing or the
-    device does not expose the metrics, `summary()` says why instead."""
-
-    def __init__(self, period_s=0.002, lead_s=0.25):
-        self.lead_s = lead_s
-        self.period_s = period_s
-        self.samples = []          # (host time, MHz)
-        self.window = None         # host times bounding the timed region
-        self.error = None
-        self._stop = threading.Event()
-        self._thread = None
-        self._handle = None
-        self._amdsmi = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            if not handles:
-                raise RuntimeError("no GPU handles")
-            self._handle = self._match(amdsmi, handles)
-            self._amdsmi = amdsmi
-            self._read()
-        except Exception as exc:   # no clock reading: reported, never fatal
-            self.error = "%s: %s" % (type(exc).__name__, exc)
-
-    @staticmethod
-    def _match(amdsmi, handles):
-        """The handle whose PCI address is cuda:0's (the first one otherwise)."""
-        try:
-            import torch
-            pr = torch.cuda.get_device_properties(0)
-            want = "%04x:%02x:%02x" % (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
-            for h in handles:
-                if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want):
-                    return h
-        except Exception:
-            pass
-        return handles[0]
-
-    def _read(self):
-        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
-        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
-        if not clks:
-            c = m.get("current_gfxclk")
-            if not isinstance(c, (int, float)):
-                raise RuntimeError("gpu metrics hold no current gfx clock")
-            clks = [c]
-        return sum(clks) / len(clks)
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append((time.perf_counter(), self._read()))
-            except Exception as exc:
-                self.error = "%s: %s" % (type(exc).__name__, exc)
-                return
-            self._stop.wait(self.period_s)
-
-    def start(self):
-        if self._amdsmi is not None:
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-
-    def stop(self):
-        self._stop.set()
-        if self._thread is not None:
-            self._thread.join()
-        if self._amdsmi is not None:
-            try:
-                self._amdsmi.amdsmi_shut_down()
-            except Exception:
-                pass
-
-    def mark(self, t0, t1):
-        """The timed region ran from host time t0 to t1."""
-        self.window = (t0, t1)
-
-    def summary(self):
-        """Samples from lead_s before the timed region to its end (the metrics
-        table refreshes every few tens of ms, so the lead keeps a short timed
-        region from reading only values taken before it, under the same
-        back-to-back load of the warmup)."""
-        xs = self.samples
-        if self.window:
-            xs = [s for s in xs if self.window[0] - self.lead_s <= s[0] <= self.window[1]]
-        if not xs:
-            return {"median_mhz": None, "samples": 0, "error": self.error or "no samples"}
-        ys = sorted(m for _, m in xs)
-        return {"median_mhz": round(ys[len(ys) // 2], 1), "min_mhz": round(ys[0], 1), "max_mhz": round(ys[-1], 1),
-                "samples": len(ys), "period_ms": self.period_s * 1e3,
-                "source": "amdsmi gpu_metrics current_gfxclks, mean over XCDs, sampled in another thread from "
-                          "%.2f s before the timed steps (the warmup's back-to-back calls) to their end"
-                          % self.lead_s}
+def clock_from_log(clocks):
+    """The clock attn_prefill_clocked logged: each workgroup's shader-clock
+    cycles over its 100 MHz ticks, as the median over workgroups and as the
+    ratio of the sums (the average over the kernel's busy time)."""
+    import numpy as np
+    c = clocks.cpu().numpy().astype(np.float64)
+    cyc, tick = c[:, 2] - c[:, 0], c[:, 3] - c[:, 1]
+    mhz = np.sort(cyc / tick * 100.0)
+    return {"median_mhz": round(float(mhz[len(mhz) // 2]), 1), "min_mhz": round(float(mhz[0]), 1),
+            "max_mhz": round(float(mhz[-1]), 1), "busy_average_mhz": round(float(cyc.sum() / tick.sum() * 100.0), 1),
+            "workgroups": int(len(mhz)),
+            "source": "attn_prefill_clocked (the same kernels): each workgroup's shader-clock counter over the fixed "
+                      "100 MHz counter from its start to its end, on the last of 10 calls run back to back right "
+                      "after the timed steps"}
 
 
 def kernel_source_hash() -> str:
@@ -565,10 +481,6 @@ def main():
     if not ok:
         print("bench: sampled parity check FAILED (%s)" % json.dumps(errstats), file=sys.stderr)
         sys.exit(1)
-    clock = ClockSampler() if not args.no_clock else None
-    if clock:
-        clock.start()
-
     t_w = time.perf_counter()
     n_w = 0
     while n_w < max(args.warmup, 1) or time.perf_counter() - t_w < args.warmup_seconds:
@@ -576,10 +488,11 @@ def main():
         n_w += 1
         if n_w % 10 == 0:
             torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
     # timed region: K steps, synchronised on both sides; HIP events on the
     # stream the kernel is launched on give the per-launch device time; the
-    # shader clock is sampled meanwhile from another thread
+    # clock the kernels run at is logged by the same kernels afterwards
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -591,9 +504,13 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    if clock:
-        clock.stop()
-        clock.mark(t0, t1)
+    # the clock the kernels run at, logged by the same kernels (plain caches)
+    clock = None
+    if not args.no_clock and not paged and not splitkv:
+        for _ in range(10):
+            _, clk_log = cpf.attn_prefill_clocked(qd, kd, vd, out=out, P=P, stream=stream)
+        torch.cuda.synchronize()
+        clock = clock_from_log(clk_log)
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
@@ -660,13 +577,13 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic_entry(name),
                      "kernel": KERNEL_NAME, "kernel_ms": round(kernel_ms, 5)},
         "launch_ms": launch_ms,
-        "clock": clock.summary() if clock else None,
+        "clock": clock,
         "cold_launch_ms": cold_ms,
         "parity": dict({"sampled_rows_ok": ok}, **(errstats or {})),
     }
-    if clock and result["clock"].get("median_mhz"):
+    if clock:
         # the same fraction against the peak at the clock the chip ran at
-        mhz = result["clock"]["median_mhz"]
+        mhz = clock["median_mhz"]
         result["roofline"]["peak_at_clock"] = round(peak * mhz / NOMINAL_MHZ, 2)
         result["roofline"]["frac_at_clock"] = round(achieved / (peak * mhz / NOMINAL_MHZ), 4)
     esz = 4 if dt == "f32" else 2

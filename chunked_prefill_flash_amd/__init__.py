@@ -21,10 +21,10 @@ import os
 import torch  # imported first so the library binds to torch's HIP runtime
 
 __all__ = ["attn_prefill", "attn_prefill_paged", "attn_prefill_paged_splitkv", "attn_prefill_rowwise",
-           "attn_prefill_splitkv",
-           "attn_prefill_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES", "splitkv_workspace", "attn_naive", "naive_workspace", "validate", "paged_validate", "plan",
-           "status_string", "library_path", "load_library", "flops", "visible_pairs", "AttnError",
-           "EXPORTED_SYMBOLS", "HQ", "HKV", "D"]
+           "attn_prefill_splitkv", "attn_prefill_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES", "splitkv_workspace",
+           "attn_naive", "naive_workspace", "validate", "paged_validate", "plan", "attn_prefill_clocked", "status_string",
+           "library_path", "load_library", "flops", "visible_pairs", "AttnError", "EXPORTED_SYMBOLS", "HQ", "HKV",
+           "D"]
 
 HQ, HKV, D = 32, 8, 64
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = ("attn_prefill", "attn_status_string", "attn_prefill_validate
                     "attn_prefill_version", "attn_prefill_paged", "attn_prefill_paged_validate",
                     "attn_prefill_rowwise", "attn_prefill_splitkv", "attn_prefill_splitkv_workspace",
                     "attn_naive", "attn_naive_workspace", "attn_prefill_splitkv_noalloc",
-                    "attn_prefill_paged_splitkv")
+                    "attn_prefill_paged_splitkv", "attn_prefill_clocked")
 
 # ATTN_NOALLOC_SCRATCH_BYTES of include/attn_prefill.h
 NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -95,6 +95,8 @@ def load_library():
     lib.attn_prefill_paged_splitkv.restype = i
     lib.attn_prefill_paged_validate.argtypes = [vp, vp, vp, vp, i, i, vp, i, i, i]
     lib.attn_prefill_paged_validate.restype = i
+    lib.attn_prefill_clocked.argtypes = [vp, vp, vp, vp, i, i, i, vp, ctypes.c_size_t, vp]
+    lib.attn_prefill_clocked.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_prefill_version.argtypes = []
@@ -209,6 +211,33 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
     if st != 0:
         raise AttnError(st, _entry)
     return out
+
+
+def attn_prefill_clocked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
+                         P: int | None = None, stream: torch.cuda.Stream | None = None):
+    """attn_prefill that also logs the clock: returns (out, clocks) with
+    clocks an int64 [workgroups][4] device tensor (not yet synchronised) of
+    (shader clock, 100 MHz counter) at each workgroup's start and end; its
+    clock in MHz is (c[:, 2] - c[:, 0]) / (c[:, 3] - c[:, 1]) * 100."""
+    C = q.shape[0]
+    if P is None:
+        P = k.shape[0] - C
+    grid = plan(C, P, q.dtype)["grid"] if C > 0 else 0
+    s = _stream(stream, q.device)
+    with torch.cuda.stream(s):
+        clocks = torch.empty((max(grid, 1), 4), dtype=torch.int64, device=q.device)
+    if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype in %s" % list(DTYPES))
+    if q.dim() != 3 or q.shape[1:] != (HQ, D) or k.shape != (P + C, HKV, D) or v.shape != k.shape:
+        raise ValueError("bad shapes q %s k %s v %s for P=%d" % (tuple(q.shape), tuple(k.shape), tuple(v.shape), P))
+    _gpu_tensors(q.device, q=q, k=k, v=v)
+    out = _out_tensor(out, C, q.device, s)
+    with torch.cuda.device(q.device):
+        st = load_library().attn_prefill_clocked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), C, P,
+                                                 DTYPES[q.dtype], clocks.data_ptr(), clocks.numel(), s.cuda_stream)
+    if st != 0:
+        raise AttnError(st, "attn_prefill_clocked")
+    return out, clocks[:grid]
 
 
 def attn_prefill_rowwise(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,

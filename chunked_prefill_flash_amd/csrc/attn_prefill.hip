@@ -109,10 +109,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-// Tile geometry for a workgroup of NW row-waves x KS key-split waves.
+// Tile geometry for a workgroup of NW row-waves x KS key-split waves with ST
+// staging buffers (2: the next tile loads while the current one is consumed;
+// 1: half the LDS, so two workgroups share a CU and overlap each other).
 //
 // LDS holds each staged K and V tile as unpadded key-major rows (256 B fp32,
-// 128 B bf16), in two stages, laid out V0 V1 K0 K1: every V operand then sits
+// 128 B bf16), in ST stages, laid out V0 V1 K0 K1: every V operand then sits
 // below 64 KiB and every K operand below 64 KiB of a per-lane base, so each
 // LDS read is one base register plus an immediate offset (the DS offset field
 // is 16 bits).  Inside a row the 16-byte chunks are permuted
@@ -120,7 +122,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 // different keys, same chunk) and the bf16 transposed V reads (16 lanes on a
 // 4-key x 16-dim block) spread over all LDS banks; unpadded rows let each
 // direct global->LDS load instruction fill 1 KiB of whole rows.
-template <typename T, int NW, int KS>
+template <typename T, int NW, int KS, int ST = 2>
 struct Geo {
     static constexpr int kNB = KS > 2 ? KS : 2;      // 32-key sub-blocks per staged tile
     static constexpr int kBK = 32 * kNB;             // keys per staged tile
@@ -130,15 +132,15 @@ struct Geo {
     static constexpr int kRowBytes = kD * Elem<T>::kBytes;
     static constexpr int kTileBytes = kBK * kRowBytes;                // one tensor, one stage
     static constexpr int kStageBytes = 2 * kTileBytes;                // K and V of one stage
-    static constexpr int kKBase = 2 * kTileBytes;                     // K0 follows V0 and V1
-    static constexpr int kKSpan = 4 * kTileBytes - kKBase;            // K0 and K1
+    static constexpr int kKBase = ST * kTileBytes;                    // K0 follows the V stages
+    static constexpr int kKSpan = ST * kTileBytes;                    // the K stages
     static_assert(2 * kTileBytes <= 65536 && kKSpan <= 65536, "LDS operand offsets must fit 16 bits");
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;             // rows per 64-lane 16 B load
     static constexpr int kLoadsPerTile = 2 * kBK / kRowsPerLoad;      // K and V
     static constexpr int kLoadsPerWave = (kLoadsPerTile + kWaves - 1) / kWaves;
     // Merge buffer for key splits: per (row-wave, split>0) wave, 34 floats/lane.
     static constexpr int kMergeBytes = KS > 1 ? NW * (KS - 1) * 34 * 64 * 4 : 0;
-    static constexpr int kLdsBytes = 2 * kStageBytes > kMergeBytes ? 2 * kStageBytes : kMergeBytes;
+    static constexpr int kLdsBytes = ST * kStageBytes > kMergeBytes ? ST * kStageBytes : kMergeBytes;
 };
 
 // Row-dependent chunk permutation (XOR code) of a staged K/V row.
@@ -167,13 +169,37 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// n / d for 0 <= n < 2^32 and a divisor d >= 1 fixed for the launch, as one
+// high multiply, a subtract, an add and two shifts (Granlund and Montgomery,
+// "Division by invariant integers using multiplication", 1994, section 4:
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
+// q = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0) with t = mulhi(m, n)).
+struct FastDiv {
+    uint32_t m;
+    int s1, s2;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return FastDiv{(uint32_t)m, l < 1 ? l : 1, l > 1 ? l - 1 : 0};
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+    const uint32_t t = __umulhi(f.m, n);
+    return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
 // Paged cache description ("FlashAttention and inference kernels", section
 // PagedAttention): position t lives at slot t % page_size of physical page
 // table[t / page_size]; kc/vc then point at [num_blocks][page_size][8][64].
+// `div` divides by page_size.
 struct PagedCache {
     const int* table;
     int page_size;
     int num_blocks;
+    FastDiv div;
 };
 
 // Key-range split across workgroups (Flash-Decoding, "FlashAttention and
@@ -193,12 +219,21 @@ enum Mode { kPlain = 0, kPaged = 1, kSplit = 2, kPagedSplit = 3 };
 // The kernel.  One workgroup = one KV group g and one or two row tiles.
 // ---------------------------------------------------------------------------
 
-template <typename T, int NW, int KS, int MODE>
-__global__ void __launch_bounds__(64 * NW * KS)
+template <typename T, int NW, int KS, int MODE, int ST = 2>
+__global__ void __launch_bounds__(64 * NW * KS, ST == 1 ? 2 : 1)
 attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
                     float* __restrict__ out, int C, int P, int n_row_tiles, int paired, PagedCache pg,
-                    KeySplit ks) {
-    using G = Geo<T, NW, KS>;
+                    KeySplit ks, unsigned long long* __restrict__ clk) {
+    static_assert(ST == 2 || (ST == 1 && MODE == 0), "one staging buffer: plain contiguous caches only");
+    // Clock log (attn_prefill_clocked; null otherwise): thread 0 stores the
+    // shader-clock counter and the fixed 100 MHz counter at the workgroup's
+    // start and end, with ordinary vector stores, so that the clock the kernel
+    // runs at can be read from the kernel itself.
+    if (clk != nullptr && threadIdx.x == 0) {
+        clk[4 * blockIdx.x] = __builtin_amdgcn_s_memtime();
+        clk[4 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+    }
+    using G = Geo<T, NW, KS, ST>;
     constexpr int kBK = G::kBK, kNB = G::kNB, kRows = G::kRows, kRB = G::kRowBytes;
     constexpr bool kF32 = sizeof(T) == 4;
     constexpr bool PAGED = (MODE & kPaged) != 0;
@@ -251,37 +286,45 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     const int pc = lane % kCPR;                     // chunk position within the row
     auto load_row = [&](int u) { return ((wid + u * G::kWaves) % (kBK / kRPL)) * kRPL + rl; };
     // Paged cache: the byte offset of every K/V row of tile t sits in LDS slot
-    // t & 1, written two tiles ahead by the first kBK threads (one table read
-    // each, in flight during a tile's math), so a lane holds no page state.
+    // t & 1, written two tiles ahead by the first kBK threads, so a lane holds
+    // no page state.  The table entry of each row goes from memory straight
+    // into LDS (a buffer load with an LDS destination, in flight during a
+    // tile's math: no register is held across it), and the row's byte offset
+    // is formed from it after the tile's vmcnt(0).
     __shared__ uint32_t pofs[PAGED ? 2 * kBK : 1];
+    __shared__ int pent[PAGED ? 2 * kBK : 1];       // table entries, by row
+    __shared__ uint32_t pslot[PAGED ? 2 * kBK : 1]; // positions within the page, by row
     constexpr uint32_t kNoRow = 0xffffffffu;        // past the cache, or a bad table entry
-    struct PageRef {
-        int ph;     // table entry (-1 past the cache)
-        int slot;   // position within the page
-    };
     // The table is read through a buffer descriptor (scalar base, 32-bit lane
     // offset), and row offsets are formed in 32 bits: the host rejects pools
     // and tables whose byte sizes do not fit them.
     const __amdgpu_buffer_rsrc_t rtab = __builtin_amdgcn_make_buffer_rsrc(
         (void*)pg.table, (short)0, PAGED ? (uint32_t)((total + pg.page_size - 1) / pg.page_size) * 4u : 0u,
         0x00020000);
-    auto fetch_page = [&](int t) {                  // key kb + t*kBK + tid; divides before the tile's math
-        const int key = kb + t * kBK + tid;
-        PageRef r{-1, 0};
-        if (tid < kBK && key < total) {
-            const int blk = key / pg.page_size;
-            r.slot = key - blk * pg.page_size;
-            r.ph = (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, (uint32_t)blk * 4u, 0, 0);
+    // The thread index is made opaque in both helpers so that nothing derived
+    // from it is hoisted out of the key loop and held in registers throughout.
+    auto fetch_page = [&](int t) {                  // row tid of tile t: its table entry and in-page slot
+        if (tid < kBK) {                            // whole waves (kBK is a multiple of 64)
+            int r = tid;
+            asm volatile("" : "+v"(r));
+            const int key = kb + t * kBK + r;
+            const uint32_t blk = fast_div((uint32_t)min(key, total - 1), pg.div);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rtab, (lds_void_t*)(pent + (t & 1) * kBK + (r & ~63)), 4,
+                                                     blk * 4u, 0, 0, 0);
+            pslot[(t & 1) * kBK + r] = key < total ? (uint32_t)key - blk * (uint32_t)pg.page_size : kNoRow;
         }
-        return r;
     };
-    auto store_offset = [&](int t, PageRef r) {
-        if (tid < kBK)
-            pofs[(t & 1) * kBK + tid] =
-                r.ph >= 0 && r.ph < pg.num_blocks
-                    ? ((uint32_t)r.ph * (uint32_t)pg.page_size + (uint32_t)r.slot) * (uint32_t)(kHKV * kRB) +
-                          (uint32_t)(g * kRB)
+    auto store_offset = [&](int t) {                // after the vmcnt(0) that covers fetch_page(t)
+        if (tid < kBK) {
+            int r = tid;
+            asm volatile("" : "+v"(r));
+            const int ph = pent[(t & 1) * kBK + r];
+            const uint32_t in_page = pslot[(t & 1) * kBK + r];
+            pofs[(t & 1) * kBK + r] =
+                in_page != kNoRow && ph >= 0 && ph < pg.num_blocks
+                    ? ((uint32_t)ph * (uint32_t)pg.page_size + in_page) * (uint32_t)(kHKV * kRB) + (uint32_t)(g * kRB)
                     : kNoRow;
+        }
     };
     auto issue_tile = [&](int t, int stage) {
         const int key0 = kb + t * kBK;
@@ -338,10 +381,11 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         const int lim = P + row;                    // this lane's query sees keys <= lim
 
         if constexpr (PAGED) {
-            const PageRef ph0 = fetch_page(0);
-            const PageRef ph1 = ntiles > 1 ? fetch_page(1) : PageRef{-1, 0};
-            store_offset(0, ph0);
-            if (ntiles > 1) store_offset(1, ph1);
+            fetch_page(0);
+            if (ntiles > 1) fetch_page(1);
+            __builtin_amdgcn_s_waitcnt(0x3f70);     // vmcnt(0): the entries have landed in LDS
+            store_offset(0);
+            if (ntiles > 1) store_offset(1);
             __syncthreads();
         }
         issue_tile(0, 0);
@@ -354,7 +398,12 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // lane); rows past the chunk read as zero.  The output is stored the
         // same way.
         const int item_rows = min(kRows, C - i0);
-        const uint32_t lane_vec = (uint32_t)(((row - i0) * kHQ + head) * kD);   // element offset in the item
+        // element offset of this lane's (row, head) in the item, formed from an
+        // opaque lane copy so it is recomputed per item rather than held
+        int lane1 = lane;
+        asm volatile("" : "+v"(lane1));
+        const uint32_t lane_vec =
+            (uint32_t)((8 * wr + ((lane1 & 31) >> 2)) * kHQ + g * kGroup + (lane1 & 3)) * kD;
         float qf[kF32 ? 32 : 1];
         bf8 qb[kF32 ? 1 : 4];
         {
@@ -598,42 +647,61 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // stage was last read before the previous barrier.
         __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile 0 has landed in LDS
         __syncthreads();
+        // One staging buffer: every tile is consumed, then the next is loaded
+        // into the same buffer; the other workgroup on the CU computes meanwhile.
+        if constexpr (ST == 1) {
+            for (int t = 0; t < ntiles; ++t) {
+                const VOps vo = prefetch_v(std::integral_constant<int, 0>{}, t);
+                consume(std::integral_constant<int, 0>{}, t, vo);
+                __syncthreads();                      // every wave is done with the tile
+                if (t + 1 < ntiles) {
+                    issue_tile(t + 1, 0);
+                    __builtin_amdgcn_s_waitcnt(0x3f70);
+                    __syncthreads();
+                }
+            }
+        }
         // Paged: the table entries of tile t+2 are read during tile t and their
         // offsets stored after its vmcnt(0), into the slot tile t's loads used
         // (every wave issued those before the previous barrier).
-        for (int t = 0; t < ntiles; t += 2) {
-            PageRef ph{-1, 0};
+        for (int t = 0; ST == 2 && t < ntiles; t += 2) {
             VOps vo = prefetch_v(std::integral_constant<int, 0>{}, t);
             if (t + 1 < ntiles) issue_tile(t + 1, 1);
             if constexpr (PAGED) {
-                if (t + 2 < ntiles) ph = fetch_page(t + 2);
+                if (t + 2 < ntiles) fetch_page(t + 2);
             }
             consume(std::integral_constant<int, 0>{}, t, vo);
             __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile t+1 has landed
             if constexpr (PAGED) {
-                if (t + 2 < ntiles) store_offset(t + 2, ph);
+                if (t + 2 < ntiles) store_offset(t + 2);
             }
             __syncthreads();
             if (t + 1 < ntiles) {
                 vo = prefetch_v(std::integral_constant<int, 1>{}, t + 1);
                 if (t + 2 < ntiles) issue_tile(t + 2, 0);
                 if constexpr (PAGED) {
-                    if (t + 3 < ntiles) ph = fetch_page(t + 3);
+                    if (t + 3 < ntiles) fetch_page(t + 3);
                 }
                 consume(std::integral_constant<int, 1>{}, t + 1, vo);
                 __builtin_amdgcn_s_waitcnt(0x3f70);
                 if constexpr (PAGED) {
-                    if (t + 3 < ntiles) store_offset(t + 3, ph);
+                    if (t + 3 < ntiles) store_offset(t + 3);
                 }
                 __syncthreads();
             }
         }
 
+        // Lane offsets used after the key loop are formed again from an opaque
+        // copy of the lane index, so they are not held (or spilled) through it.
+        int lane2 = lane;
+        asm volatile("" : "+v"(lane2));
+        const uint32_t out_vec = (uint32_t)((8 * wr + ((lane2 & 31) >> 2)) * kHQ + g * kGroup + (lane2 & 3)) * kD;
+
         // ---- merge key splits (log-sum-exp), in LDS ----
         if constexpr (KS > 1) {
             float* mb = reinterpret_cast<float*>(lds_raw);
             if (wp > 0 && wave_active) {
-                float* dst = mb + (size_t)((wr * (KS - 1) + wp - 1) * 34) * 64 + lane;
+                float* dst = mb + (size_t)((wr * (KS - 1) + wp - 1) * 34) * 64 + lane2;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     dst[r * 64] = o0[r];
@@ -646,7 +714,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             if (wp == 0 && wave_active) {
 #pragma unroll
                 for (int sp = 1; sp < KS; ++sp) {
-                    const float* src = mb + (size_t)((wr * (KS - 1) + sp - 1) * 34) * 64 + lane;
+                    const float* src = mb + (size_t)((wr * (KS - 1) + sp - 1) * 34) * 64 + lane2;
                     const float m2 = src[32 * 64];
                     const float l2 = src[33 * 64];
                     const float mx = fmaxf(m, m2);
@@ -673,7 +741,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)item, (short)0, (uint32_t)item_rows * kHQ * kD * 4, 0x00020000);
             auto st4 = [&](uint32_t elem, f4 x) {
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro, (lane_vec + elem) * 4, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro, (out_vec + elem) * 4, 0, 0);
             };
             if constexpr (kF32) {
                 // rows 8a+4hh+j: dims 16a+8hh+2j (o0), +1 (o1)
@@ -712,6 +780,10 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             if (row < C) store_o(out + (size_t)i0 * kHQ * kD, inv);
         }
         __syncthreads();   // LDS is reused by the next work item
+    }
+    if (clk != nullptr && threadIdx.x == 0) {
+        clk[4 * blockIdx.x + 2] = __builtin_amdgcn_s_memtime();
+        clk[4 * blockIdx.x + 3] = __builtin_amdgcn_s_memrealtime();
     }
 }
 
@@ -900,28 +972,6 @@ __device__ __forceinline__ void load_row8(__amdgpu_buffer_rsrc_t r, uint32_t off
     }
 }
 
-// n / d for 0 <= n < 2^32 and a divisor d >= 1 fixed for the launch, as one
-// high multiply, a subtract, an add and two shifts (Granlund and Montgomery,
-// "Division by invariant integers using multiplication", 1994, section 4:
-// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
-// q = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0) with t = mulhi(m, n)).
-struct FastDiv {
-    uint32_t m;
-    int s1, s2;
-};
-
-FastDiv make_fastdiv(uint32_t d) {
-    int l = 0;
-    while ((1ull << l) < d) ++l;
-    const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
-    return FastDiv{(uint32_t)m, l < 1 ? l : 1, l > 1 ? l - 1 : 0};
-}
-
-__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
-    const uint32_t t = __umulhi(f.m, n);
-    return (t + ((n - t) >> f.s1)) >> f.s2;
-}
-
 // sum over the 8 consecutive lanes of a key slot; every lane ends with the
 // same bits (each step adds the same two values in either order)
 __device__ __forceinline__ float slot_sum8(float x) {
@@ -938,7 +988,7 @@ __device__ __forceinline__ float slot_sum8(float x) {
 template <bool PAGED>
 __global__ void __launch_bounds__(64 * kDecWaves)
 attn_decode_split_kernel(const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
-                         float* __restrict__ part, int P, int len, int n, PagedCache pg, FastDiv pdiv) {
+                         float* __restrict__ part, int P, int len, int n, PagedCache pg) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -979,14 +1029,14 @@ attn_decode_split_kernel(const float* __restrict__ q, const float* __restrict__ 
         0x00020000);
     // byte offset of this lane's 8 dims of position `key` in the pools
     auto row_offset = [&](int key, int entry) -> uint32_t {
-        const uint32_t blk = fast_div((uint32_t)key, pdiv);
+        const uint32_t blk = fast_div((uint32_t)key, pg.div);
         const uint32_t in_page = (uint32_t)key - blk * (uint32_t)pg.page_size;
         return entry >= 0 && entry < pg.num_blocks
                    ? (((uint32_t)entry * (uint32_t)pg.page_size + in_page) * kHKV + g) * kRowBytes + 32u * ds
                    : pool_bytes;
     };
     auto table_entry = [&](int key) -> int {   // key < kend, or the entry is not used
-        const uint32_t blk = fast_div((uint32_t)min(key, kend - 1), pdiv);
+        const uint32_t blk = fast_div((uint32_t)min(key, kend - 1), pg.div);
         return (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, blk * 4u, 0, 0);
     };
 
@@ -1236,7 +1286,7 @@ naive_pv_kernel(const float* __restrict__ S, const float* __restrict__ v, float*
 // ---------------------------------------------------------------------------
 // Host side: argument checks, launch plan, dispatch.
 // ---------------------------------------------------------------------------
-enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3, kV_decode = 4, kV_8x2 = 5 };
+enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3, kV_decode = 4, kV_8x2 = 5, kV_1x4s1 = 7 };
 
 struct Plan {
     int rows, ks, grid, threads, per_wg, bk, lds, variant, n_row_tiles, paired;
@@ -1245,9 +1295,9 @@ struct Plan {
 
 // pair < 0: pair tiles i and n-1-i when that still leaves a workgroup per CU;
 // otherwise pair iff pair != 0.
-template <typename T, int NW, int KS>
+template <typename T, int NW, int KS, int ST = 2>
 Plan make_plan(int C, int variant, int pair = -1) {
-    using G = Geo<T, NW, KS>;
+    using G = Geo<T, NW, KS, ST>;
     Plan p{};
     p.rows = G::kRows;
     p.ks = KS;
@@ -1307,8 +1357,19 @@ Plan choose_plan(int C, int P, bool paged) {
         constexpr double kItem = 32.0 * 52.0;
         const ShapeCost c32 = shape_cost(C, P, 32, 1.0, kItem), c16 = shape_cost(C, P, 16, 0.92, kItem),
                         c8 = shape_cost(C, P, 8, 0.68, kItem);
+        // One staging buffer with 8-row items, unpaired: two workgroups share a
+        // CU (512 slots), each nearly as fast as alone since the other computes
+        // while it waits on its loads.  Measured against the two-stage 8-row
+        // and unpaired 16-row plans it wins when its items fill whole rounds
+        // of the 512 slots (T=512 +16%; T=1536 and C=1500 P=100 +4%) and loses
+        // where the last round is partial (T=768 -11%) and to paired 16-row
+        // items (T=1024 -10%) and on long prefixes (C=512 P=15872 -3%); plain
+        // caches and short prefixes (P <= C/4) only.
+        const int rem = (8 * ((C + 7) / 8)) % 512;
+        const bool one_stage = !paged && P <= C / 4 && (rem == 0 || rem >= 440);
         if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired);
-        else if (c16.t <= c8.t) p = make_plan<T, 2, 4>(C, kV_2x4, c16.paired);
+        else if (c16.t <= c8.t && (c16.paired || !one_stage)) p = make_plan<T, 2, 4>(C, kV_2x4, c16.paired);
+        else if (one_stage) p = make_plan<T, 1, 4, 1>(C, kV_1x4s1, 0);
         else p = make_plan<T, 1, 4>(C, kV_1x4, c8.paired);
     } else {
         // two 16-row workgroups fit a CU, so pairing them into 256 workgroups
@@ -1326,33 +1387,36 @@ Plan plan_for(int C, int P, attn_dtype_t dtype, bool paged) {
     return dtype == ATTN_DTYPE_BF16 ? choose_plan<__bf16>(C, P, paged) : choose_plan<float>(C, P, paged);
 }
 
-template <typename T, int NW, int KS, int MODE>
+template <typename T, int NW, int KS, int MODE, int ST = 2>
 hipError_t launch(const Plan& p, const void* q, const void* k, const void* v, float* out, int C, int P,
-                  PagedCache pg, KeySplit ksp, hipStream_t stream) {
+                  PagedCache pg, KeySplit ksp, unsigned long long* clk, hipStream_t stream) {
     const T* qq = static_cast<const T*>(q);
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
     int n_row_tiles = p.n_row_tiles, paired = p.paired;
-    void* args[] = {&qq, &kk, &vv, &out, &C, &P, &n_row_tiles, &paired, &pg, &ksp};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_prefill_kernel<T, NW, KS, MODE>), dim3(p.grid),
+    void* args[] = {&qq, &kk, &vv, &out, &C, &P, &n_row_tiles, &paired, &pg, &ksp, &clk};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_prefill_kernel<T, NW, KS, MODE, ST>), dim3(p.grid),
                            dim3(p.threads), args, 0, stream);
 }
 
 template <typename T, int MODE>
 hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, float* out, int C, int P,
-                    PagedCache pg, KeySplit ksp, hipStream_t stream) {
+                    PagedCache pg, KeySplit ksp, hipStream_t stream, unsigned long long* clk = nullptr) {
     switch (p.variant) {
         case kV_4x2:
             if constexpr ((MODE & kSplit) != 0) return hipErrorInvalidValue;   // never planned
-            else return launch<T, 4, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
-        case kV_2x4: return launch<T, 2, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
+            else return launch<T, 4, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
+        case kV_2x4: return launch<T, 2, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
+        case kV_1x4s1:   // planned for fp32 plain caches only
+            if constexpr (MODE != kPlain || sizeof(T) != 4) return hipErrorInvalidValue;
+            else return launch<T, 1, 4, MODE, 1>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
         case kV_8x2:   // planned for bf16 contiguous caches only
             if constexpr (MODE != kPlain || sizeof(T) != 2) return hipErrorInvalidValue;
-            else return launch<T, 8, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
+            else return launch<T, 8, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
         case kV_4x4:   // planned for fp32 only, never with key splits
             if constexpr ((MODE & kSplit) != 0 || sizeof(T) != 4) return hipErrorInvalidValue;
-            else return launch<T, 4, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
-        default: return launch<T, 1, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, stream);
+            else return launch<T, 4, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
+        default: return launch<T, 1, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
     }
 }
 
@@ -1442,9 +1506,8 @@ attn_status_t launch_splitkv(const Plan& p, const void* q, const void* kCache, c
     int len = p.split_len, n = p.splits;
     hipError_t e;
     if (p.variant == kV_decode) {
-        FastDiv pdiv = make_fastdiv((uint32_t)pg.page_size);
         void* dargs[] = {const_cast<void**>(&q), const_cast<void**>(&kCache), const_cast<void**>(&vCache), &part, &P,
-                         &len, &n, &pg, &pdiv};
+                         &len, &n, &pg};
         const void* fn = paged ? reinterpret_cast<const void*>(&attn_decode_split_kernel<true>)
                                : reinterpret_cast<const void*>(&attn_decode_split_kernel<false>);
         e = hipLaunchKernel(fn, dim3(p.grid), dim3(p.threads), dargs, 0, stream);
@@ -1512,6 +1575,28 @@ attn_status_t attn_prefill(const void* q, const void* kCache, const void* vCache
     const hipError_t e = dtype == ATTN_DTYPE_BF16
                              ? dispatch<__bf16, kPlain>(p, q, kCache, vCache, out, C, P, none, nosplit, stream)
                              : dispatch<float, kPlain>(p, q, kCache, vCache, out, C, P, none, nosplit, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+attn_status_t attn_prefill_clocked(const void* q, const void* kCache, const void* vCache, float* out, int C, int P,
+                                   attn_dtype_t dtype, unsigned long long* clocks, size_t clockCount,
+                                   hipStream_t stream) {
+    const attn_status_t st = attn_prefill_validate(q, kCache, vCache, out, C, P, dtype);
+    if (st != ATTN_OK || C == 0) return st;
+    const Plan p = plan_for(C, P, dtype, false);
+    if (!clocks) return ATTN_ERR_NULL_PTR;
+    if (reinterpret_cast<uintptr_t>(clocks) & 7u) return ATTN_ERR_MISALIGNED;
+    if (clockCount < 4 * (size_t)p.grid) return ATTN_ERR_WORKSPACE;
+    const size_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
+    const size_t nq = (size_t)C * kHQ * kD, nkv = ((size_t)P + C) * kHKV * kD, nc = 32 * (size_t)p.grid;
+    if (overlaps(clocks, nc, q, nq * esz) || overlaps(clocks, nc, kCache, nkv * esz) ||
+        overlaps(clocks, nc, vCache, nkv * esz) || overlaps(clocks, nc, out, nq * 4))
+        return ATTN_ERR_ALIAS;
+    const PagedCache none{nullptr, 1, 0, {}};
+    const KeySplit nosplit{nullptr, 0, 0};
+    const hipError_t e = dtype == ATTN_DTYPE_BF16
+                             ? dispatch<__bf16, kPlain>(p, q, kCache, vCache, out, C, P, none, nosplit, stream, clocks)
+                             : dispatch<float, kPlain>(p, q, kCache, vCache, out, C, P, none, nosplit, stream, clocks);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -1659,7 +1744,7 @@ attn_status_t attn_prefill_paged(const void* q, const void* kPages, const void* 
         attn_prefill_paged_validate(q, kPages, vPages, blockTable, numBlocks, pageSize, out, C, P, dtype);
     if (st != ATTN_OK || C == 0) return st;
     const Plan p = plan_for(C, P, dtype, true);
-    const PagedCache pg{blockTable, pageSize, numBlocks};
+    const PagedCache pg{blockTable, pageSize, numBlocks, make_fastdiv((uint32_t)pageSize)};
     const KeySplit nosplit{nullptr, 0, 0};
     const hipError_t e = dtype == ATTN_DTYPE_BF16
                              ? dispatch<__bf16, kPaged>(p, q, kPages, vPages, out, C, P, pg, nosplit, stream)
@@ -1688,7 +1773,7 @@ attn_status_t attn_prefill_paged_splitkv(const void* q, const void* kPages, cons
         overlaps(workspace, need, out, nq * 4))
         return ATTN_ERR_ALIAS;
     return launch_splitkv(p, q, kPages, vPages, out, C, P, dtype, static_cast<float*>(workspace),
-                          PagedCache{blockTable, pageSize, numBlocks}, stream);
+                          PagedCache{blockTable, pageSize, numBlocks, make_fastdiv((uint32_t)pageSize)}, stream);
 }
 
 const char* attn_status_string(attn_status_t s) {

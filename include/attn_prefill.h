@@ -92,6 +92,30 @@ typedef enum {
 attn_status_t attn_prefill(const void* q, const void* kCache, const void* vCache, float* out,
                            int C, int P, attn_dtype_t dtype, hipStream_t stream);
 
+/*
+ * attn_prefill_clocked -- attn_prefill (the same kernels, launch plan and
+ * result) that also logs the clock it runs at, for reporting throughput
+ * against the peak at that clock as well as the nominal one: thread 0 of every
+ * workgroup stores the shader-clock counter and the fixed 100 MHz counter when
+ * the workgroup starts and when it ends.
+ *
+ *   clocks      device memory of at least clockCount unsigned 64-bit values,
+ *               8-byte aligned, not overlapping any tensor; workgroup w writes
+ *               clocks[4w .. 4w+3] = shader clock at start, 100 MHz counter at
+ *               start, shader clock at end, 100 MHz counter at end
+ *   clockCount  at least 4 x the workgroups of the launch (plan[2] of
+ *               attn_prefill_plan for the same C, P, dtype with paged = 0)
+ *   other arguments as for attn_prefill
+ *
+ * The clock of workgroup w over its life is (clocks[4w+2] - clocks[4w]) /
+ * (clocks[4w+3] - clocks[4w+1]) * 100 MHz.  Returns as attn_prefill, plus
+ * ATTN_ERR_NULL_PTR / ATTN_ERR_MISALIGNED / ATTN_ERR_ALIAS for clocks and
+ * ATTN_ERR_WORKSPACE when clockCount is too small.
+ */
+attn_status_t attn_prefill_clocked(const void* q, const void* kCache, const void* vCache, float* out,
+                                   int C, int P, attn_dtype_t dtype, unsigned long long* clocks,
+                                   size_t clockCount, hipStream_t stream);
+
 /* Static, NUL-terminated name of a status code ("ATTN_OK", ...). */
 const char* attn_status_string(attn_status_t status);
 

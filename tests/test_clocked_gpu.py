@@ -1,0 +1,44 @@
+"""GPU check of attn_prefill_clocked, the entry point the benchmark reads its
+clock from: the same result as attn_prefill bit for bit, and a clock log in
+which every workgroup started before it ended and ran at a plausible MI355X
+shader clock (a few hundred MHz idle to about 2.4 GHz)."""
+import numpy as np
+import pytest
+import torch
+
+import chunked_prefill_flash_amd as cpf
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("C,P,dtype", [(2048, 2048, torch.float32), (512, 0, torch.float32),
+                                       (100, 3000, torch.float32), (4096, 100, torch.bfloat16)])
+def test_clocked_call_matches_and_logs_a_plausible_clock(C, P, dtype):
+    q, k, v = synth.case_plain(C, P, 9500 + C)
+    qd, kd, vd = (torch.from_numpy(x).cuda().to(dtype) for x in (q, k, v))
+    want = cpf.attn_prefill(qd, kd, vd, P=P)
+    got, clocks = cpf.attn_prefill_clocked(qd, kd, vd, P=P)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+    c = clocks.cpu().numpy().astype(np.float64)
+    assert c.shape == (cpf.plan(C, P, dtype)["grid"], 4)
+    assert np.all(c[:, 2] > c[:, 0]) and np.all(c[:, 3] > c[:, 1])
+    mhz = (c[:, 2] - c[:, 0]) / (c[:, 3] - c[:, 1]) * 100.0
+    assert np.all((mhz > 100) & (mhz < 2600)), (mhz.min(), mhz.max())
+
+
+def test_clocked_rejects_a_short_clock_buffer():
+    lib = cpf.load_library()
+    C, P = 64, 64
+    q = torch.zeros(C, 32, 64, device="cuda")
+    k = torch.zeros(P + C, 8, 64, device="cuda")
+    out = torch.zeros(C, 32, 64, device="cuda")
+    grid = cpf.plan(C, P)["grid"]
+    buf = torch.zeros(4 * grid, dtype=torch.int64, device="cuda")
+    args = (q.data_ptr(), k.data_ptr(), k.data_ptr(), out.data_ptr(), C, P, 0)
+    assert lib.attn_prefill_clocked(*args, buf.data_ptr(), 4 * grid - 1, None) == 7
+    assert lib.attn_prefill_clocked(*args, None, 4 * grid, None) == 2
+    assert lib.attn_prefill_clocked(*args, buf.data_ptr() + 4, 4 * grid, None) == 4
+    assert lib.attn_prefill_clocked(*args, out.data_ptr(), 4 * grid, None) == 6
+    torch.cuda.synchronize()
