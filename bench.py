@@ -125,7 +125,41 @@ def rocprof_passes(name, outdir):
 PRODUCT_KERNELS = ("attn_prefill_kernel", "attn_decode_split_kernel", "attn_merge_splits_kernel")
 
 
+def _demangled_args(rest):
+    """Template arguments of an Itanium-mangled kernel name's suffix, for the
+    few forms these kernels use (float, __bf16, ints, bools)."""
+    args, i = [], 0
+    if not rest.startswith("I"):
+        return None
+    i = 1
+    while i < len(rest) and rest[i] != "E":
+        if rest.startswith("DF16b", i):
+            args.append("__bf16")
+            i += 5
+        elif rest[i] == "f":
+            args.append("float")
+            i += 1
+        elif rest.startswith("Lb", i):
+            args.append("true" if rest[i + 2] == "1" else "false")
+            i += 4
+        elif rest.startswith("Li", i):
+            j = rest.index("E", i)
+            args.append(rest[i + 2:j])
+            i = j + 1
+        else:
+            return None
+    return args
+
+
 def _short_kernel(name):
+    if name.startswith("_Z"):
+        for k in PRODUCT_KERNELS + ("attn_rowwise_kernel", "naive_scores_kernel", "naive_softmax_kernel",
+                                    "naive_pv_kernel"):
+            at = name.find(k)
+            if at >= 0:
+                args = _demangled_args(name[at + len(k):])
+                return k + ("<%s>" % ", ".join(args) if args else "")
+        return name[:70]
     n = name.replace("(anonymous namespace)::", "").replace("void ", "")
     for k in PRODUCT_KERNELS + ("attn_rowwise_kernel", "naive_scores_kernel", "naive_softmax_kernel",
                                 "naive_pv_kernel"):
@@ -204,7 +238,9 @@ def summarize_rocprof(name, outdir, profiles_dir=None):
             if k.split("<")[0] in PRODUCT_KERNELS:
                 per_call += float(r["AverageNs"]) / 1e3
         md.append("")
-        if decode:
+        if per_call <= 0:
+            md.append("(no product kernel found in this trace)")
+        elif decode:
             md.append("Per call (the product kernels' averages summed): %.2f us -> %.1f GB/s over %d algorithmic "
                       "bytes (%.1f%% of 8 TB/s)." % (per_call, alg / per_call / 1e3, alg,
                                                      alg / per_call / 1e3 / HBM_PEAK_GBS * 100))
