@@ -63,3 +63,38 @@ def test_splitkv_decode_in_a_graph():
         cpf.attn_prefill_splitkv(qd, kd, vd, out=out, P=P, workspace=ws)
     scratch = torch.empty(1 << 20, device=dev())
     replay_and_compare(graph, out, want, lambda: scratch.normal_())
+
+
+def test_noalloc_decode_in_a_graph():
+    """The no-alloc entry point is meant for callers that capture graphs: its
+    partials live in the library's fixed array, so capture needs no buffer
+    but the inputs and out."""
+    C, P = 1, 12000
+    q, k, v = synth.case_plain(C, P, 8300)
+    qd, kd, vd = g(q), g(k), g(v)
+    want = torch.empty((C, 32, 64), device=dev())
+    cpf.attn_prefill_splitkv_noalloc(qd, kd, vd, want, P=P)
+    torch.cuda.synchronize()
+    out = torch.empty_like(want)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cpf.attn_prefill_splitkv_noalloc(qd, kd, vd, out, P=P)
+    scratch = torch.empty(1 << 20, device=dev())
+    replay_and_compare(graph, out, want, lambda: scratch.normal_())
+
+
+def test_paged_splitkv_decode_in_a_graph():
+    C, P = 1, 7000
+    q, k, v = synth.case_plain(C, P, 8400)
+    kp, vp, table = synth.to_pages(k, v, 16, 8401)
+    qd, kpd, vpd, tabd = g(q), g(kp), g(vp), torch.from_numpy(table).to(dev())
+    need, _ = cpf.splitkv_workspace(C, P)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev())
+    want = cpf.attn_prefill_paged_splitkv(qd, kpd, vpd, tabd, P, workspace=ws).clone()
+    out = torch.empty_like(want)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cpf.attn_prefill_paged_splitkv(qd, kpd, vpd, tabd, P, out=out, workspace=ws)
+    scratch = torch.empty(1 << 20, device=dev())
+    replay_and_compare(graph, out, want, lambda: scratch.uniform_())

@@ -93,15 +93,16 @@ def test_shape(entry, dtype, C, P, page):
 def test_wide_sweep_sampled_rows():
     """A wider seeded sweep checked on sampled rows (first, last, six drawn, the
     planted ones; all 32 heads): entry point among contiguous, paged (pages of
-    1-256 positions), split-KV and per-row; C log-uniform in [1, 2500], P in
-    [0, 6000] (0 one time in five).  CPF_SWEEP_CASES sets the number of cases
-    (default 200, a few seconds; 3000 take under two minutes)."""
+    1-256 positions), split-KV, paged split-KV, split-KV without a workspace
+    and per-row; C log-uniform in [1, 2500], P in [0, 6000] (0 one time in
+    five).  CPF_SWEEP_CASES sets the number of cases (default 200, a few
+    seconds; 3000 take under two minutes)."""
     n = int(os.environ.get("CPF_SWEEP_CASES", "200"))
     r = synth.uniform53(778, 8 * n)
     bad = []
     for t in range(n):
         u = r[8 * t: 8 * t + 8]
-        entry = ("prefill", "paged", "splitkv", "rowwise")[int(u[0] * 4) % 4]
+        entry = ("prefill", "paged", "splitkv", "rowwise", "paged_splitkv", "noalloc")[int(u[0] * 6) % 6]
         dtype = "bf16" if u[1] < 0.5 else "f32"
         C = max(1, int(round(math.exp(u[2] * math.log(2500)))))
         P = 0 if u[3] < 0.2 else int(round(math.exp(u[4] * math.log(6000))))
@@ -111,6 +112,8 @@ def test_wide_sweep_sampled_rows():
         seed = 50000 + t
         q, k, v, plants = synth.case_planted_chunk(C, P, seed, 3)
         tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+        if entry == "noalloc" and cpf.splitkv_workspace(C, P, tdt)[0] > cpf.NOALLOC_SCRATCH_BYTES:
+            entry = "splitkv"   # beyond the fixed scratch array
         out = torch.full((C, HQ, D), float("nan"), device="cuda")
         if entry == "prefill":
             cpf.attn_prefill(_gpu(q, dtype), _gpu(k, dtype), _gpu(v, dtype), out=out, P=P)
@@ -120,6 +123,14 @@ def test_wide_sweep_sampled_rows():
             kp, vp, table = synth.to_pages(k, v, page, seed + 5)
             cpf.attn_prefill_paged(_gpu(q, dtype), _gpu(kp, dtype), _gpu(vp, dtype),
                                    torch.from_numpy(table).cuda(), P, out=out)
+        elif entry == "paged_splitkv":
+            kp, vp, table = synth.to_pages(k, v, page, seed + 5)
+            need, _ = cpf.splitkv_workspace(C, P, tdt)
+            ws = torch.full((need // 4 + 4,), float("nan"), device="cuda")
+            cpf.attn_prefill_paged_splitkv(_gpu(q, dtype), _gpu(kp, dtype), _gpu(vp, dtype),
+                                           torch.from_numpy(table).cuda(), P, out=out, workspace=ws)
+        elif entry == "noalloc":
+            cpf.attn_prefill_splitkv_noalloc(_gpu(q, dtype), _gpu(k, dtype), _gpu(v, dtype), out, P=P)
         else:
             need, _ = cpf.splitkv_workspace(C, P, tdt)
             ws = torch.full((need // 4 + 4,), float("nan"), device="cuda")
