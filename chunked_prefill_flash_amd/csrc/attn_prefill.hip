@@ -1483,9 +1483,14 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_addr[kMaxDevices] = {};
 
-attn_status_t scratch_address(void** addr) {
+attn_status_t scratch_address(hipStream_t stream, void** addr) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_LAUNCH;
+    // the kernels run on the stream's device: it must be the current one,
+    // whose copy of the array is the one looked up here
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return ATTN_ERR_LAUNCH;
+    if (sdev != dev) return ATTN_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_addr[dev]) {
         void* p = nullptr;
@@ -1641,7 +1646,7 @@ attn_status_t attn_prefill_splitkv_noalloc(const void* q, const void* kCache, co
     const Plan p = split_plan(C, P, dtype);
     if (split_workspace_bytes(p, C) > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_TOO_LARGE;
     void* ws = nullptr;
-    const attn_status_t sa = scratch_address(&ws);
+    const attn_status_t sa = scratch_address(stream, &ws);
     if (sa != ATTN_OK) return sa;
     return launch_splitkv(p, q, kCache, vCache, out, C, P, dtype, static_cast<float*>(ws), PagedCache{nullptr, 1, 0},
                           stream);

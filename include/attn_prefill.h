@@ -217,7 +217,8 @@ attn_status_t attn_prefill_splitkv(const void* q, const void* kCache, const void
  * when attn_prefill_splitkv_workspace() for (C, P, dtype) exceeds
  * ATTN_NOALLOC_SCRATCH_BYTES (for example C above about 1980 rows); use
  * attn_prefill or attn_prefill_splitkv there.  ATTN_ERR_LAUNCH also when the
- * array's address cannot be obtained.
+ * array's address cannot be obtained, and ATTN_ERR_INVALID_ARG (nothing
+ * enqueued) when `stream` belongs to another device than the current one.
  */
 attn_status_t attn_prefill_splitkv_noalloc(const void* q, const void* kCache, const void* vCache, float* out,
                                            int C, int P, attn_dtype_t dtype, hipStream_t stream);
