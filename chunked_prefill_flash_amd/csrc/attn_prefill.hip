@@ -194,13 +194,35 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
 // Paged cache description ("FlashAttention and inference kernels", section
 // PagedAttention): position t lives at slot t % page_size of physical page
 // table[t / page_size]; kc/vc then point at [num_blocks][page_size][8][64].
-// `div` divides by page_size.
+// `div` divides by page_size; `shift` is log2(page_size) when that is a
+// power of two (then a shift and a mask replace the division), else -1.
 struct PagedCache {
     const int* table;
     int page_size;
     int num_blocks;
     FastDiv div;
+    int shift;
 };
+
+PagedCache make_paged(const int* table, int page_size, int num_blocks) {
+    int shift = -1;
+    if ((page_size & (page_size - 1)) == 0) {
+        shift = 0;
+        while ((1 << shift) < page_size) ++shift;
+    }
+    return PagedCache{table, page_size, num_blocks, make_fastdiv((uint32_t)page_size), shift};
+}
+
+// Page index, in-page slot and first position of a page's slot (page * page_size + slot).
+__device__ __forceinline__ uint32_t page_index(uint32_t key, const PagedCache& pg) {
+    return pg.shift >= 0 ? key >> pg.shift : fast_div(key, pg.div);
+}
+__device__ __forceinline__ uint32_t page_slot(uint32_t key, uint32_t blk, const PagedCache& pg) {
+    return pg.shift >= 0 ? key & (uint32_t)(pg.page_size - 1) : key - blk * (uint32_t)pg.page_size;
+}
+__device__ __forceinline__ uint32_t pool_position(uint32_t page, uint32_t slot, const PagedCache& pg) {
+    return pg.shift >= 0 ? (page << pg.shift) | slot : page * (uint32_t)pg.page_size + slot;
+}
 
 // Key-range split across workgroups (Flash-Decoding, "FlashAttention and
 // inference kernels"): workgroup split s covers keys [s*len, (s+1)*len) of
@@ -239,7 +261,11 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     constexpr bool PAGED = (MODE & kPaged) != 0;
     constexpr bool SPLIT = (MODE & kSplit) != 0;
 
-    __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[G::kLdsBytes];
+    // One LDS object: K/V stages (reused by the key-split merge), then, for a
+    // paged cache, the row offsets of two tiles.  A second __shared__ array
+    // would make the compiler wait for every HBM->LDS load in flight before
+    // each LDS read of the staged tiles.
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[G::kLdsBytes + (PAGED ? 2 * kBK * 4 : 0)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -286,14 +312,13 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     const int pc = lane % kCPR;                     // chunk position within the row
     auto load_row = [&](int u) { return ((wid + u * G::kWaves) % (kBK / kRPL)) * kRPL + rl; };
     // Paged cache: the byte offset of every K/V row of tile t sits in LDS slot
-    // t & 1, written two tiles ahead by the first kBK threads, so a lane holds
-    // no page state.  The table entry of each row goes from memory straight
-    // into LDS (a buffer load with an LDS destination, in flight during a
-    // tile's math: no register is held across it), and the row's byte offset
-    // is formed from it after the tile's vmcnt(0).
-    __shared__ uint32_t pofs[PAGED ? 2 * kBK : 1];
-    __shared__ int pent[PAGED ? 2 * kBK : 1];       // table entries, by row
-    __shared__ uint32_t pslot[PAGED ? 2 * kBK : 1]; // positions within the page, by row
+    // t & 1, written two tiles ahead by the first kBK threads, so a lane that
+    // issues a row's loads holds no page state.  Those threads read the table
+    // entry of their row of tile t+2 into a register while tile t is consumed
+    // (a plain load: a load into LDS there would make every LDS read of the
+    // tile wait for the loads in flight) and store the row's byte offset after
+    // the tile's vmcnt(0).
+    uint32_t* const pofs = reinterpret_cast<uint32_t*>(lds_raw + G::kLdsBytes);   // [2][kBK]
     constexpr uint32_t kNoRow = 0xffffffffu;        // past the cache, or a bad table entry
     // The table is read through a buffer descriptor (scalar base, 32-bit lane
     // offset), and row offsets are formed in 32 bits: the host rejects pools
@@ -303,26 +328,25 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         0x00020000);
     // The thread index is made opaque in both helpers so that nothing derived
     // from it is hoisted out of the key loop and held in registers throughout.
-    auto fetch_page = [&](int t) {                  // row tid of tile t: its table entry and in-page slot
+    auto fetch_entry = [&](int t) {                 // table entry of row tid of tile t (first kBK threads)
+        int ent = 0;
         if (tid < kBK) {                            // whole waves (kBK is a multiple of 64)
             int r = tid;
             asm volatile("" : "+v"(r));
-            const int key = kb + t * kBK + r;
-            const uint32_t blk = fast_div((uint32_t)min(key, total - 1), pg.div);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rtab, (lds_void_t*)(pent + (t & 1) * kBK + (r & ~63)), 4,
-                                                     blk * 4u, 0, 0, 0);
-            pslot[(t & 1) * kBK + r] = key < total ? (uint32_t)key - blk * (uint32_t)pg.page_size : kNoRow;
+            const int key = kb + t * kBK + r;       // past the table: the load reads zero
+            ent = (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, page_index((uint32_t)key, pg) * 4u, 0, 0);
         }
+        return ent;
     };
-    auto store_offset = [&](int t) {                // after the vmcnt(0) that covers fetch_page(t)
+    auto store_offset = [&](int t, int ent) {       // after the vmcnt(0) that covers fetch_entry(t)
         if (tid < kBK) {
             int r = tid;
             asm volatile("" : "+v"(r));
-            const int ph = pent[(t & 1) * kBK + r];
-            const uint32_t in_page = pslot[(t & 1) * kBK + r];
+            const int key = kb + t * kBK + r;
+            const uint32_t in_page = page_slot((uint32_t)key, page_index((uint32_t)key, pg), pg);
             pofs[(t & 1) * kBK + r] =
-                in_page != kNoRow && ph >= 0 && ph < pg.num_blocks
-                    ? ((uint32_t)ph * (uint32_t)pg.page_size + in_page) * (uint32_t)(kHKV * kRB) + (uint32_t)(g * kRB)
+                key < total && (uint32_t)ent < (uint32_t)pg.num_blocks
+                    ? pool_position((uint32_t)ent, in_page, pg) * (uint32_t)(kHKV * kRB) + (uint32_t)(g * kRB)
                     : kNoRow;
         }
     };
@@ -381,11 +405,10 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         const int lim = P + row;                    // this lane's query sees keys <= lim
 
         if constexpr (PAGED) {
-            fetch_page(0);
-            if (ntiles > 1) fetch_page(1);
-            __builtin_amdgcn_s_waitcnt(0x3f70);     // vmcnt(0): the entries have landed in LDS
-            store_offset(0);
-            if (ntiles > 1) store_offset(1);
+            const int e0 = fetch_entry(0);
+            const int e1 = ntiles > 1 ? fetch_entry(1) : 0;
+            store_offset(0, e0);
+            if (ntiles > 1) store_offset(1, e1);
             __syncthreads();
         }
         issue_tile(0, 0);
@@ -667,25 +690,26 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         for (int t = 0; ST == 2 && t < ntiles; t += 2) {
             VOps vo = prefetch_v(std::integral_constant<int, 0>{}, t);
             if (t + 1 < ntiles) issue_tile(t + 1, 1);
+            int ent = 0;
             if constexpr (PAGED) {
-                if (t + 2 < ntiles) fetch_page(t + 2);
+                if (t + 2 < ntiles) ent = fetch_entry(t + 2);
             }
             consume(std::integral_constant<int, 0>{}, t, vo);
             __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile t+1 has landed
             if constexpr (PAGED) {
-                if (t + 2 < ntiles) store_offset(t + 2);
+                if (t + 2 < ntiles) store_offset(t + 2, ent);
             }
             __syncthreads();
             if (t + 1 < ntiles) {
                 vo = prefetch_v(std::integral_constant<int, 1>{}, t + 1);
                 if (t + 2 < ntiles) issue_tile(t + 2, 0);
                 if constexpr (PAGED) {
-                    if (t + 3 < ntiles) fetch_page(t + 3);
+                    if (t + 3 < ntiles) ent = fetch_entry(t + 3);
                 }
                 consume(std::integral_constant<int, 1>{}, t + 1, vo);
                 __builtin_amdgcn_s_waitcnt(0x3f70);
                 if constexpr (PAGED) {
-                    if (t + 3 < ntiles) store_offset(t + 3);
+                    if (t + 3 < ntiles) store_offset(t + 3, ent);
                 }
                 __syncthreads();
             }
@@ -1029,15 +1053,13 @@ attn_decode_split_kernel(const float* __restrict__ q, const float* __restrict__ 
         0x00020000);
     // byte offset of this lane's 8 dims of position `key` in the pools
     auto row_offset = [&](int key, int entry) -> uint32_t {
-        const uint32_t blk = fast_div((uint32_t)key, pg.div);
-        const uint32_t in_page = (uint32_t)key - blk * (uint32_t)pg.page_size;
-        return entry >= 0 && entry < pg.num_blocks
-                   ? (((uint32_t)entry * (uint32_t)pg.page_size + in_page) * kHKV + g) * kRowBytes + 32u * ds
+        const uint32_t in_page = page_slot((uint32_t)key, page_index((uint32_t)key, pg), pg);
+        return (uint32_t)entry < (uint32_t)pg.num_blocks
+                   ? (pool_position((uint32_t)entry, in_page, pg) * kHKV + g) * kRowBytes + 32u * ds
                    : pool_bytes;
     };
     auto table_entry = [&](int key) -> int {   // key < kend, or the entry is not used
-        const uint32_t blk = fast_div((uint32_t)min(key, kend - 1), pg.div);
-        return (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, blk * 4u, 0, 0);
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(rtab, page_index((uint32_t)min(key, kend - 1), pg) * 4u, 0, 0);
     };
 
     constexpr int kStep = 8 * kDecWaves;    // keys between a wave's consecutive chunks
@@ -1374,12 +1396,12 @@ Plan choose_plan(int C, int P, bool paged) {
     } else {
         // two 16-row workgroups fit a CU, so pairing them into 256 workgroups
         // would leave half the slots empty: they stay unpaired
-        p = C >= 2048 ? (C >= 4096 && !paged ? make_plan<T, 8, 2>(C, kV_8x2, shape_cost(C, P, 64, 1.0, 64.0 * 177.0).paired)
+        p = C >= 2048 ? (C >= 4096 ? make_plan<T, 8, 2>(C, kV_8x2, shape_cost(C, P, 64, 1.0, 64.0 * 177.0).paired)
                                              : make_plan<T, 4, 2>(C, kV_4x2))
             : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4, 0)
                        : make_plan<T, 1, 4>(C, kV_1x4);
     }
-    p.lds += 4 * (paged ? 2 * p.bk : 1);   // the page-offset table (one word when unused)
+    if (paged) p.lds += 4 * 2 * p.bk;   // the row offsets of two tiles
     return p;
 }
 
@@ -1410,8 +1432,8 @@ hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, 
         case kV_1x4s1:   // planned for fp32 plain caches only
             if constexpr (MODE != kPlain || sizeof(T) != 4) return hipErrorInvalidValue;
             else return launch<T, 1, 4, MODE, 1>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
-        case kV_8x2:   // planned for bf16 contiguous caches only
-            if constexpr (MODE != kPlain || sizeof(T) != 2) return hipErrorInvalidValue;
+        case kV_8x2:   // planned for bf16 only, never with key splits
+            if constexpr ((MODE & kSplit) != 0 || sizeof(T) != 2) return hipErrorInvalidValue;
             else return launch<T, 8, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
         case kV_4x4:   // planned for fp32 only, never with key splits
             if constexpr ((MODE & kSplit) != 0 || sizeof(T) != 4) return hipErrorInvalidValue;
@@ -1453,7 +1475,6 @@ Plan split_plan(int C, int P, attn_dtype_t dtype) {
                      : (dtype == ATTN_DTYPE_BF16 ? make_plan<__bf16, 2, 4>(C, kV_2x4) : make_plan<float, 2, 4>(C, kV_2x4));
     p.paired = 0;
     p.per_wg = 1;
-    p.lds += 4;   // the unused page-offset word
     const int total = P + C;
     const int base = p.n_row_tiles * kHKV;
     constexpr int kTargetWorkgroups = 256;
@@ -1636,7 +1657,7 @@ attn_status_t attn_prefill_splitkv(const void* q, const void* kCache, const void
         overlaps(workspace, need, vCache, nkv * esz) || overlaps(workspace, need, out, nq * 4))
         return ATTN_ERR_ALIAS;
     return launch_splitkv(p, q, kCache, vCache, out, C, P, dtype, static_cast<float*>(workspace),
-                          PagedCache{nullptr, 1, 0}, stream);
+                          make_paged(nullptr, 1, 0), stream);
 }
 
 attn_status_t attn_prefill_splitkv_noalloc(const void* q, const void* kCache, const void* vCache, float* out,
@@ -1648,7 +1669,7 @@ attn_status_t attn_prefill_splitkv_noalloc(const void* q, const void* kCache, co
     void* ws = nullptr;
     const attn_status_t sa = scratch_address(stream, &ws);
     if (sa != ATTN_OK) return sa;
-    return launch_splitkv(p, q, kCache, vCache, out, C, P, dtype, static_cast<float*>(ws), PagedCache{nullptr, 1, 0},
+    return launch_splitkv(p, q, kCache, vCache, out, C, P, dtype, static_cast<float*>(ws), make_paged(nullptr, 1, 0),
                           stream);
 }
 
@@ -1749,7 +1770,7 @@ attn_status_t attn_prefill_paged(const void* q, const void* kPages, const void* 
         attn_prefill_paged_validate(q, kPages, vPages, blockTable, numBlocks, pageSize, out, C, P, dtype);
     if (st != ATTN_OK || C == 0) return st;
     const Plan p = plan_for(C, P, dtype, true);
-    const PagedCache pg{blockTable, pageSize, numBlocks, make_fastdiv((uint32_t)pageSize)};
+    const PagedCache pg = make_paged(blockTable, pageSize, numBlocks);
     const KeySplit nosplit{nullptr, 0, 0};
     const hipError_t e = dtype == ATTN_DTYPE_BF16
                              ? dispatch<__bf16, kPaged>(p, q, kPages, vPages, out, C, P, pg, nosplit, stream)
@@ -1778,7 +1799,7 @@ attn_status_t attn_prefill_paged_splitkv(const void* q, const void* kPages, cons
         overlaps(workspace, need, out, nq * 4))
         return ATTN_ERR_ALIAS;
     return launch_splitkv(p, q, kPages, vPages, out, C, P, dtype, static_cast<float*>(workspace),
-                          PagedCache{blockTable, pageSize, numBlocks, make_fastdiv((uint32_t)pageSize)}, stream);
+                          make_paged(blockTable, pageSize, numBlocks), stream);
 }
 
 const char* attn_status_string(attn_status_t s) {

@@ -85,17 +85,20 @@ def test_paged_full_size_c2048_p2048():
     check(got, ref, "f32", what="paged C=P=2048")
 
 
-@pytest.mark.parametrize("C,P", [(600, 1000), (1100, 300)])
-def test_paged_equals_contiguous_bitwise(C, P):
+@pytest.mark.parametrize("C,P,dtype", [(600, 1000, "f32"), (1100, 300, "f32"), (2048, 500, "bf16"),
+                                     (4096, 300, "bf16")])
+def test_paged_equals_contiguous_bitwise(C, P, dtype):
     """Same launch plan, same arithmetic: the paged path must reproduce the
-    contiguous path bit for bit (16-row and 32-row work items)."""
+    contiguous path bit for bit (fp32 16-row and 32-row work items; bf16
+    32-row and 64-row ones)."""
     q, k, v = synth.case_plain(C, P, 5400 + C)
     kp, vp, table = synth.to_pages(k, v, 16, 5401 + C)
-    pp, pc = cpf.plan(C, P, paged=True), cpf.plan(C, P)
-    assert pp.pop("lds_bytes") == pc.pop("lds_bytes") - 4 + 2 * 4 * pc["keys_per_tile"]   # + page-offset table
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    pp, pc = cpf.plan(C, P, tdt, paged=True), cpf.plan(C, P, tdt)
+    assert pp.pop("lds_bytes") == pc.pop("lds_bytes") + 2 * 4 * pc["keys_per_tile"]   # + row offsets of two tiles
     assert pp == pc
-    paged = run_paged(q, kp, vp, table, P, "f32")
-    contig = cpf.attn_prefill(to_gpu(q, "f32"), to_gpu(k, "f32"), to_gpu(v, "f32"), P=P).cpu().numpy()
+    paged = run_paged(q, kp, vp, table, P, dtype)
+    contig = cpf.attn_prefill(to_gpu(q, dtype), to_gpu(k, dtype), to_gpu(v, dtype), P=P).cpu().numpy()
     assert np.array_equal(paged.view(np.uint32), contig.view(np.uint32))
 
 
