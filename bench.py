@@ -78,17 +78,39 @@ NOMINAL_MHZ = 2400.0   # the clock the published peaks assume
 def clock_from_log(clocks):
     """The clock attn_prefill_clocked logged: each workgroup's shader-clock
     cycles over its 100 MHz ticks, as the median over workgroups and as the
-    ratio of the sums (the average over the kernel's busy time)."""
+    ratio of the sums (the average over the kernel's busy time); and where a
+    workgroup's time goes, from the phase marks (medians over workgroups, each
+    phase's cycles over that workgroup's own clock)."""
     import numpy as np
     c = clocks.cpu().numpy().astype(np.float64)
     cyc, tick = c[:, 2] - c[:, 0], c[:, 3] - c[:, 1]
-    mhz = np.sort(cyc / tick * 100.0)
+    mhz_wg = cyc / tick * 100.0
+    mhz = np.sort(mhz_wg)
+
+    def med_us(a, b, rows=None):
+        sel = np.ones(len(c), bool) if rows is None else rows
+        if not sel.any():
+            return None
+        return round(float(np.median((c[sel, b] - c[sel, a]) / mhz_wg[sel])), 2)
+
+    two = c[:, 7] != 0                       # workgroups with a second work item
+    phases = {
+        "first_item_prologue": med_us(0, 4),   # start until its Q and first K/V tile have landed
+        "first_item_key_loop": med_us(4, 5),
+        "first_item_epilogue": med_us(5, 6),   # key-split merge, output store, barrier
+        "second_item_prologue": med_us(6, 7, two),
+        "second_item_rest": med_us(7, 2, two),
+        "workgroup": med_us(0, 2),
+        "workgroups_with_two_items": int(two.sum()),
+        "kernel_span": round(float((c[:, 3].max() - c[:, 1].min()) / 100.0), 2),
+        "start_spread": round(float((c[:, 1].max() - c[:, 1].min()) / 100.0), 2),
+    }
     return {"median_mhz": round(float(mhz[len(mhz) // 2]), 1), "min_mhz": round(float(mhz[0]), 1),
             "max_mhz": round(float(mhz[-1]), 1), "busy_average_mhz": round(float(cyc.sum() / tick.sum() * 100.0), 1),
-            "workgroups": int(len(mhz)),
+            "workgroups": int(len(mhz)), "phases_us": phases,
             "source": "attn_prefill_clocked (the same kernels): each workgroup's shader-clock counter over the fixed "
                       "100 MHz counter from its start to its end, on the last of 10 calls run back to back right "
-                      "after the timed steps"}
+                      "after the timed steps; phases are the medians over workgroups of the spans between its marks"}
 
 
 def kernel_source_hash() -> str:

@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = ("attn_prefill", "attn_status_string", "attn_prefill_validate
 
 # ATTN_NOALLOC_SCRATCH_BYTES of include/attn_prefill.h
 NOALLOC_SCRATCH_BYTES = 16 << 20
+CLOCK_WORDS = 8                  # ATTN_CLOCK_WORDS: clock-log words per workgroup
 
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_NULL_PTR", 3: "ATTN_ERR_UNSUPPORTED_DTYPE",
@@ -216,16 +217,20 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
 def attn_prefill_clocked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
                          P: int | None = None, stream: torch.cuda.Stream | None = None):
     """attn_prefill that also logs the clock: returns (out, clocks) with
-    clocks an int64 [workgroups][4] device tensor (not yet synchronised) of
-    (shader clock, 100 MHz counter) at each workgroup's start and end; its
-    clock in MHz is (c[:, 2] - c[:, 0]) / (c[:, 3] - c[:, 1]) * 100."""
+    clocks an int64 [workgroups][CLOCK_WORDS] device tensor (not yet
+    synchronised, zero where a mark was not written): (shader clock, 100 MHz
+    counter) at each workgroup's start [0, 1] and end [2, 3], and the shader
+    clock when its first work item's first tile is in LDS [4], when that
+    item's key loop is done [5] and its output stored [6], and when a second
+    item's first tile is in LDS [7].  A workgroup's clock in MHz is
+    (c[:, 2] - c[:, 0]) / (c[:, 3] - c[:, 1]) * 100."""
     C = q.shape[0]
     if P is None:
         P = k.shape[0] - C
     grid = plan(C, P, q.dtype)["grid"] if C > 0 else 0
     s = _stream(stream, q.device)
     with torch.cuda.stream(s):
-        clocks = torch.empty((max(grid, 1), 4), dtype=torch.int64, device=q.device)
+        clocks = torch.zeros((max(grid, 1), CLOCK_WORDS), dtype=torch.int64, device=q.device)
     if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype in %s" % list(DTYPES))
     if q.dim() != 3 or q.shape[1:] != (HQ, D) or k.shape != (P + C, HKV, D) or v.shape != k.shape:

@@ -79,6 +79,7 @@ constexpr int kHQ = ATTN_NUM_Q_HEADS;   // 32
 constexpr int kHKV = ATTN_NUM_KV_HEADS; // 8
 constexpr int kD = ATTN_HEAD_DIM;       // 64
 constexpr int kGroup = kHQ / kHKV;      // 4
+constexpr int kClockWords = ATTN_CLOCK_WORDS;   // clock-log words per workgroup
 
 // log2(e) / 8: scores become base-2 exponents with the 1/8 scale applied.
 constexpr float kScaleLog2 = 0.18033688011112042f;
@@ -251,9 +252,15 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     // shader-clock counter and the fixed 100 MHz counter at the workgroup's
     // start and end, with ordinary vector stores, so that the clock the kernel
     // runs at can be read from the kernel itself.
+    // Clock log (attn_prefill_clocked): thread 0 stores the shader-clock
+    // counter at the phase marks of the first two work items, and the fixed
+    // 100 MHz counter at the start and end.
+    auto mark = [&](int slot) {
+        if (clk != nullptr && threadIdx.x == 0) clk[kClockWords * blockIdx.x + slot] = __builtin_amdgcn_s_memtime();
+    };
     if (clk != nullptr && threadIdx.x == 0) {
-        clk[4 * blockIdx.x] = __builtin_amdgcn_s_memtime();
-        clk[4 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+        clk[kClockWords * blockIdx.x] = __builtin_amdgcn_s_memtime();
+        clk[kClockWords * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
     }
     using G = Geo<T, NW, KS, ST>;
     constexpr int kBK = G::kBK, kNB = G::kNB, kRows = G::kRows, kRB = G::kRowBytes;
@@ -670,6 +677,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // stage was last read before the previous barrier.
         __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile 0 has landed in LDS
         __syncthreads();
+        if (it < 2) mark(it == 0 ? 4 : 7);       // the item's first tile is in LDS
         // One staging buffer: every tile is consumed, then the next is loaded
         // into the same buffer; the other workgroup on the CU computes meanwhile.
         if constexpr (ST == 1) {
@@ -715,6 +723,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             }
         }
 
+        if (it == 0) mark(5);                    // the first item's key loop is done
         // Lane offsets used after the key loop are formed again from an opaque
         // copy of the lane index, so they are not held (or spilled) through it.
         int lane2 = lane;
@@ -804,10 +813,11 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             if (row < C) store_o(out + (size_t)i0 * kHQ * kD, inv);
         }
         __syncthreads();   // LDS is reused by the next work item
+        if (it == 0) mark(6);                    // the first item's output is stored
     }
     if (clk != nullptr && threadIdx.x == 0) {
-        clk[4 * blockIdx.x + 2] = __builtin_amdgcn_s_memtime();
-        clk[4 * blockIdx.x + 3] = __builtin_amdgcn_s_memrealtime();
+        clk[kClockWords * blockIdx.x + 2] = __builtin_amdgcn_s_memtime();
+        clk[kClockWords * blockIdx.x + 3] = __builtin_amdgcn_s_memrealtime();
     }
 }
 
@@ -1596,7 +1606,7 @@ attn_status_t attn_prefill(const void* q, const void* kCache, const void* vCache
     const attn_status_t st = attn_prefill_validate(q, kCache, vCache, out, C, P, dtype);
     if (st != ATTN_OK || C == 0) return st;
     const Plan p = plan_for(C, P, dtype, false);
-    const PagedCache none{nullptr, 1, 0};
+    const PagedCache none = make_paged(nullptr, 1, 0);
     const KeySplit nosplit{nullptr, 0, 0};
     const hipError_t e = dtype == ATTN_DTYPE_BF16
                              ? dispatch<__bf16, kPlain>(p, q, kCache, vCache, out, C, P, none, nosplit, stream)
@@ -1612,13 +1622,13 @@ attn_status_t attn_prefill_clocked(const void* q, const void* kCache, const void
     const Plan p = plan_for(C, P, dtype, false);
     if (!clocks) return ATTN_ERR_NULL_PTR;
     if (reinterpret_cast<uintptr_t>(clocks) & 7u) return ATTN_ERR_MISALIGNED;
-    if (clockCount < 4 * (size_t)p.grid) return ATTN_ERR_WORKSPACE;
+    if (clockCount < kClockWords * (size_t)p.grid) return ATTN_ERR_WORKSPACE;
     const size_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
-    const size_t nq = (size_t)C * kHQ * kD, nkv = ((size_t)P + C) * kHKV * kD, nc = 32 * (size_t)p.grid;
+    const size_t nq = (size_t)C * kHQ * kD, nkv = ((size_t)P + C) * kHKV * kD, nc = 8 * kClockWords * (size_t)p.grid;
     if (overlaps(clocks, nc, q, nq * esz) || overlaps(clocks, nc, kCache, nkv * esz) ||
         overlaps(clocks, nc, vCache, nkv * esz) || overlaps(clocks, nc, out, nq * 4))
         return ATTN_ERR_ALIAS;
-    const PagedCache none{nullptr, 1, 0, {}};
+    const PagedCache none = make_paged(nullptr, 1, 0);
     const KeySplit nosplit{nullptr, 0, 0};
     const hipError_t e = dtype == ATTN_DTYPE_BF16
                              ? dispatch<__bf16, kPlain>(p, q, kCache, vCache, out, C, P, none, nosplit, stream, clocks)

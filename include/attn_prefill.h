@@ -94,24 +94,33 @@ attn_status_t attn_prefill(const void* q, const void* kCache, const void* vCache
 
 /*
  * attn_prefill_clocked -- attn_prefill (the same kernels, launch plan and
- * result) that also logs the clock it runs at, for reporting throughput
- * against the peak at that clock as well as the nominal one: thread 0 of every
- * workgroup stores the shader-clock counter and the fixed 100 MHz counter when
- * the workgroup starts and when it ends.
+ * result) that also logs the clock it runs at and where each workgroup's time
+ * goes, for reporting throughput against the peak at that clock as well as
+ * the nominal one: thread 0 of every workgroup stores counters at fixed marks.
  *
  *   clocks      device memory of at least clockCount unsigned 64-bit values,
  *               8-byte aligned, not overlapping any tensor; workgroup w writes
- *               clocks[4w .. 4w+3] = shader clock at start, 100 MHz counter at
- *               start, shader clock at end, 100 MHz counter at end
- *   clockCount  at least 4 x the workgroups of the launch (plan[2] of
- *               attn_prefill_plan for the same C, P, dtype with paged = 0)
+ *               the ATTN_CLOCK_WORDS values from clocks[ATTN_CLOCK_WORDS * w]:
+ *                 [0] shader clock at start      [1] 100 MHz counter at start
+ *                 [2] shader clock at end        [3] 100 MHz counter at end
+ *                 [4] shader clock when its first work item's first K/V tile
+ *                     is in LDS (the item's Q and tile loads have landed)
+ *                 [5] shader clock when that item's key loop is done
+ *                 [6] shader clock when that item's output is stored
+ *                 [7] shader clock when the second work item's first tile
+ *                     is in LDS; not written when there is no second item
+ *   clockCount  at least ATTN_CLOCK_WORDS x the workgroups of the launch
+ *               (plan[2] of attn_prefill_plan for the same C, P, dtype with
+ *               paged = 0)
  *   other arguments as for attn_prefill
  *
- * The clock of workgroup w over its life is (clocks[4w+2] - clocks[4w]) /
- * (clocks[4w+3] - clocks[4w+1]) * 100 MHz.  Returns as attn_prefill, plus
- * ATTN_ERR_NULL_PTR / ATTN_ERR_MISALIGNED / ATTN_ERR_ALIAS for clocks and
- * ATTN_ERR_WORKSPACE when clockCount is too small.
+ * The clock of workgroup w over its life is ([2] - [0]) / ([3] - [1]) *
+ * 100 MHz; a phase in seconds is its shader-clock difference over that clock.
+ * Returns as attn_prefill, plus ATTN_ERR_NULL_PTR / ATTN_ERR_MISALIGNED /
+ * ATTN_ERR_ALIAS for clocks and ATTN_ERR_WORKSPACE when clockCount is too
+ * small.
  */
+#define ATTN_CLOCK_WORDS 8
 attn_status_t attn_prefill_clocked(const void* q, const void* kCache, const void* vCache, float* out,
                                    int C, int P, attn_dtype_t dtype, unsigned long long* clocks,
                                    size_t clockCount, hipStream_t stream);

@@ -49,6 +49,14 @@ def test_every_declared_symbol_is_exported(lib):
     assert declared_functions() <= exported
 
 
+def test_binding_constants_match_the_header():
+    src = open(os.path.join(os.path.dirname(__file__), "..", "include", "attn_prefill.h")).read()
+    defs = dict(re.findall(r"#define (ATTN_\w+) \(?([^)\n]*)\)?", src))
+    assert int(defs["ATTN_CLOCK_WORDS"]) == cpf.CLOCK_WORDS
+    base, shift = re.fullmatch(r"(\d+)u << (\d+)", defs["ATTN_NOALLOC_SCRATCH_BYTES"]).groups()
+    assert int(base) << int(shift) == cpf.NOALLOC_SCRATCH_BYTES
+
+
 def test_library_contains_gfx950_code():
     blob = open(cpf.library_path(), "rb").read()
     assert b"gfx950" in blob
