@@ -118,10 +118,12 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 // 128 B bf16), in ST stages, laid out V0 V1 K0 K1: every V operand then sits
 // below 64 KiB and every K operand below 64 KiB of a per-lane base, so each
 // LDS read is one base register plus an immediate offset (the DS offset field
-// is 16 bits).  Inside a row the 16-byte chunks are permuted
-// by XOR with a per-row code so that the MFMA operand reads (32 lanes on 32
-// different keys, same chunk) and the bf16 transposed V reads (16 lanes on a
-// 4-key x 16-dim block) spread over all LDS banks; unpadded rows let each
+// is 16 bits).  Inside a row the 16-byte chunks are permuted by XOR with a
+// per-row code, one for K rows and one for V rows, so that the operand reads
+// spread over all LDS banks: a 16-byte K read serves 16 lanes (16 keys, the
+// same logical chunk) per LDS cycle, whose 16-byte slots must then all differ
+// modulo 256 bytes; the V reads (fp32: 8 bytes per lane; bf16: transposed
+// 4-key x 16-dim blocks) have their own pattern.  Unpadded rows let each
 // direct global->LDS load instruction fill 1 KiB of whole rows.
 template <typename T, int NW, int KS, int ST = 2>
 struct Geo {
@@ -144,7 +146,24 @@ struct Geo {
     static constexpr int kLdsBytes = ST * kStageBytes > kMergeBytes ? ST * kStageBytes : kMergeBytes;
 };
 
-// Row-dependent chunk permutation (XOR code) of a staged K/V row.
+// Row-dependent chunk permutations (XOR codes) of staged rows.  A 16-byte
+// K operand read serves 16 lanes (16 keys at the same logical chunk) per LDS
+// cycle of 256 bytes, so their 16-byte slots must all differ modulo 256
+// bytes.  fp32: a row is one such cycle of 16 chunks, so each row of a
+// 16-key group gets its own code.  bf16: two 128-byte rows share a cycle, in
+// its two halves, so each row pair gets its own code.  Both depend on the row
+// modulo 16, and every stage, tile and sub-block offset is a multiple of 16
+// rows.
+template <typename T>
+__device__ __forceinline__ int k_code(int r) {
+    if constexpr (sizeof(T) == 4) {
+        return r & 15;
+    } else {
+        return (r >> 1) & 7;
+    }
+}
+
+// V rows: the code of the operand reads' row within an 8-row block.
 template <typename T>
 __device__ __forceinline__ int chunk_code(int r) {
     if constexpr (sizeof(T) == 4) {
@@ -255,10 +274,13 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     // Clock log (attn_prefill_clocked): thread 0 stores the shader-clock
     // counter at the phase marks of the first two work items, and the fixed
     // 100 MHz counter at the start and end.
+    // Only the plain kernels are ever launched with a log.
+    constexpr bool kLog = MODE == kPlain;
     auto mark = [&](int slot) {
-        if (clk != nullptr && threadIdx.x == 0) clk[kClockWords * blockIdx.x + slot] = __builtin_amdgcn_s_memtime();
+        if (kLog && clk != nullptr && threadIdx.x == 0)
+            clk[kClockWords * blockIdx.x + slot] = __builtin_amdgcn_s_memtime();
     };
-    if (clk != nullptr && threadIdx.x == 0) {
+    if (kLog && clk != nullptr && threadIdx.x == 0) {
         clk[kClockWords * blockIdx.x] = __builtin_amdgcn_s_memtime();
         clk[kClockWords * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
     }
@@ -376,7 +398,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             if (G::kLoadsPerTile % G::kWaves != 0 && i >= G::kLoadsPerTile) break;
             const int tensor = i / (kBK / kRPL);
             const int row = load_row(u);
-            const int lc = pc ^ chunk_code<T>(row);     // logical chunk stored at position pc
+            const int lc = pc ^ (tensor ? chunk_code<T>(row) : k_code<T>(row));   // logical chunk at position pc
             uint32_t voff;
             if constexpr (PAGED) {
                 const uint32_t ro = pofs[(t & 1) * kBK + row];
@@ -464,9 +486,10 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         float l = 0.f;           // this lane's share of the running denominator
 
         // ---- per-lane LDS offsets of the MFMA operands (swizzle folded in) ----
-        // The XOR code of a row depends only on the row index mod 8, and every
-        // stage, tile and sub-block offset is a multiple of 8 rows, so each lane's
-        // operand addresses are a handful of fixed offsets plus immediates.
+        // The XOR codes depend only on the row index mod 16 (K) or mod 8 (V),
+        // and every stage, tile and sub-block offset is a multiple of 16 rows
+        // (V reads step by 8 rows), so each lane's operand addresses are a
+        // handful of fixed offsets plus immediates.
         //  fp32 K: chunk 8*hh + c of row n           (c = 0..7)
         //  fp32 V: dwords 2n, 2n+1 of row 4*hh + q   (q = 0..3; row + 8*(t/4))
         //  bf16 K: chunk 2*st + hh of row n          (st = 0..3)
@@ -475,7 +498,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         int voff[kF32 ? 4 : 2];
         if constexpr (kF32) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) koff[c] = G::kKBase + n * kRB + (((8 * hh + c) ^ chunk_code<T>(n)) * 16);
+            for (int c = 0; c < 8; ++c) koff[c] = G::kKBase + n * kRB + (((8 * hh + c) ^ k_code<T>(n)) * 16);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int r = 4 * hh + q4;
@@ -483,7 +506,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             }
         } else {
 #pragma unroll
-            for (int st = 0; st < 4; ++st) koff[st] = G::kKBase + n * kRB + (((2 * st + hh) ^ chunk_code<T>(n)) * 16);
+            for (int st = 0; st < 4; ++st) koff[st] = G::kKBase + n * kRB + (((2 * st + hh) ^ k_code<T>(n)) * 16);
             const int grp = (lane >> 4) & 1;
             const int j = lane & 15;
             const int r = 4 * hh + (j >> 2);            // row within an 8-row block
@@ -815,7 +838,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         __syncthreads();   // LDS is reused by the next work item
         if (it == 0) mark(6);                    // the first item's output is stored
     }
-    if (clk != nullptr && threadIdx.x == 0) {
+    if (kLog && clk != nullptr && threadIdx.x == 0) {
         clk[kClockWords * blockIdx.x + 2] = __builtin_amdgcn_s_memtime();
         clk[kClockWords * blockIdx.x + 3] = __builtin_amdgcn_s_memrealtime();
     }
