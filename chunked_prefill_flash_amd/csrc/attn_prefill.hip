@@ -267,13 +267,11 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     float* __restrict__ out, int C, int P, int n_row_tiles, int paired, PagedCache pg,
                     KeySplit ks, unsigned long long* __restrict__ clk) {
     static_assert(ST == 2 || (ST == 1 && MODE == 0), "one staging buffer: plain contiguous caches only");
-    // Clock log (attn_prefill_clocked; null otherwise): thread 0 stores the
-    // shader-clock counter and the fixed 100 MHz counter at the workgroup's
-    // start and end, with ordinary vector stores, so that the clock the kernel
-    // runs at can be read from the kernel itself.
-    // Clock log (attn_prefill_clocked): thread 0 stores the shader-clock
-    // counter at the phase marks of the first two work items, and the fixed
-    // 100 MHz counter at the start and end.
+    // Clock log (attn_prefill_clocked; null otherwise): thread 0 stores, with
+    // ordinary vector stores, the shader-clock counter and the fixed 100 MHz
+    // counter at the workgroup's start and end, and the shader clock at the
+    // phase marks of its first two work items, so that the clock the kernel
+    // runs at and where its time goes can be read from the kernel itself.
     // Only the plain kernels are ever launched with a log.
     constexpr bool kLog = MODE == kPlain;
     auto mark = [&](int slot) {
@@ -317,10 +315,18 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
 
     int items[2];
     int nitems = 1;
-    if (paired) {
+    if (paired == 1) {
         items[0] = n_row_tiles - 1 - slot;  // the heavier tile first
         items[1] = slot;
         nitems = items[1] != items[0] ? 2 : 1;
+    } else if (paired == 2) {
+        // one item per workgroup, all resident at once two per CU: the first
+        // half of the slots takes the heavy tiles in descending order and the
+        // second half the light ones ascending, so a CU's two workgroups (slots
+        // s and s + half) carry tiles n-1-s and s
+        const int half = (n_row_tiles + 1) / 2;
+        items[0] = slot < half ? n_row_tiles - 1 - slot : slot - half;
+        items[1] = items[0];
     } else {
         items[0] = n_row_tiles - 1 - slot;  // heaviest tiles are launched first
         items[1] = items[0];
@@ -342,11 +348,9 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     auto load_row = [&](int u) { return ((wid + u * G::kWaves) % (kBK / kRPL)) * kRPL + rl; };
     // Paged cache: the byte offset of every K/V row of tile t sits in LDS slot
     // t & 1, written two tiles ahead by the first kBK threads, so a lane that
-    // issues a row's loads holds no page state.  Those threads read the table
+    // issues a row's loads holds no page state.  Those threads load the table
     // entry of their row of tile t+2 into a register while tile t is consumed
-    // (a plain load: a load into LDS there would make every LDS read of the
-    // tile wait for the loads in flight) and store the row's byte offset after
-    // the tile's vmcnt(0).
+    // and store the row's byte offset after the tile's vmcnt(0).
     uint32_t* const pofs = reinterpret_cast<uint32_t*>(lds_raw + G::kLdsBytes);   // [2][kBK]
     constexpr uint32_t kNoRow = 0xffffffffu;        // past the cache, or a bad table entry
     // The table is read through a buffer descriptor (scalar base, 32-bit lane
@@ -1344,7 +1348,8 @@ naive_pv_kernel(const float* __restrict__ S, const float* __restrict__ v, float*
 enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3, kV_decode = 4, kV_8x2 = 5, kV_1x4s1 = 7 };
 
 struct Plan {
-    int rows, ks, grid, threads, per_wg, bk, lds, variant, n_row_tiles, paired;
+    int rows, ks, grid, threads, per_wg, bk, lds, variant, n_row_tiles;
+    int paired;   // 0: one item per workgroup, heaviest first; 1: tiles i and n-1-i; 2: heavy/light halves
     int splits, split_len;   // key-range splits across workgroups (0: none)
 };
 
@@ -1434,6 +1439,13 @@ Plan choose_plan(int C, int P, bool paged) {
             : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4, 0)
                        : make_plan<T, 1, 4>(C, kV_1x4);
     }
+    // Unpaired plans that run two workgroups per CU (fp32 with one staging
+    // buffer, every bf16 shape but the 64-row one) and fit in one round of
+    // 512 resident workgroups: heavy and light tiles side by side on each CU
+    // (T=512 fp32 +7%, C=1024 P=0 bf16 +8%, P=1024 +3.5%); over several
+    // rounds the heaviest-first order does better (T=1536 fp32: -6%).
+    const bool two_per_cu = sizeof(T) == 4 ? p.variant == kV_1x4s1 : p.variant != kV_8x2;
+    if (!p.paired && two_per_cu && p.grid <= 2 * 256) p.paired = 2;
     if (paged) p.lds += 4 * 2 * p.bk;   // the row offsets of two tiles
     return p;
 }
