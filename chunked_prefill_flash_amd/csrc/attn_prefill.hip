@@ -261,8 +261,10 @@ enum Mode { kPlain = 0, kPaged = 1, kSplit = 2, kPagedSplit = 3 };
 // The kernel.  One workgroup = one KV group g and one or two row tiles.
 // ---------------------------------------------------------------------------
 
+// One staging buffer: two workgroups per CU, so at least 2 * NW * KS / 4 waves
+// per SIMD (the second bound is waves per execution unit).
 template <typename T, int NW, int KS, int MODE, int ST = 2>
-__global__ void __launch_bounds__(64 * NW * KS, ST == 1 ? 2 : 1)
+__global__ void __launch_bounds__(64 * NW * KS, ST == 1 ? NW * KS / 2 : 1)
 attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
                     float* __restrict__ out, int C, int P, int n_row_tiles, int paired, PagedCache pg,
                     KeySplit ks, unsigned long long* __restrict__ clk) {
@@ -433,8 +435,12 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         const bool wave_active = i0w < C;
         const int w_first = P + i0w;                // visible limit of the wave's first row
         const int w_last = P + min(i0w + 7, C - 1); // visible limit of its last valid row
-        const int row = i0w + (n >> 2);
-        const int head = g * kGroup + (n & 3);
+        // from an opaque lane copy, so that nothing lane-derived is held
+        // across the item loop
+        int lane0 = lane;
+        asm volatile("" : "+v"(lane0));
+        const int row = i0w + ((lane0 & 31) >> 2);
+        const int head = g * kGroup + (lane0 & 3);
         const int lim = P + row;                    // this lane's query sees keys <= lim
 
         if constexpr (PAGED) {
@@ -1345,7 +1351,7 @@ naive_pv_kernel(const float* __restrict__ S, const float* __restrict__ v, float*
 // ---------------------------------------------------------------------------
 // Host side: argument checks, launch plan, dispatch.
 // ---------------------------------------------------------------------------
-enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3, kV_decode = 4, kV_8x2 = 5, kV_1x4s1 = 7 };
+enum Variant { kV_4x2 = 0, kV_2x4 = 1, kV_1x4 = 2, kV_4x4 = 3, kV_decode = 4, kV_8x2 = 5, kV_1x4s1 = 7, kV_2x4s1 = 8 };
 
 struct Plan {
     int rows, ks, grid, threads, per_wg, bk, lds, variant, n_row_tiles;
@@ -1427,7 +1433,13 @@ Plan choose_plan(int C, int P, bool paged) {
         // caches and short prefixes (P <= C/4) only.
         const int rem = (8 * ((C + 7) / 8)) % 512;
         const bool one_stage = !paged && P <= C / 4 && (rem == 0 || rem >= 440);
-        if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired);
+        // 16-row items with one staging buffer, two workgroups per CU (four
+        // waves per SIMD instead of the two of a 16-row workgroup alone), where
+        // they fill the 512 slots in one round: C = 961..1024 (+4-9% over the
+        // paired two-stage 16-row items at P = 0..4096; -2% at P = 16384)
+        const bool one_stage16 = !paged && C > 960 && C <= 1024 && P <= 4 * C;
+        if (one_stage16) p = make_plan<T, 2, 4, 1>(C, kV_2x4s1, 0);
+        else if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired);
         else if (c16.t <= c8.t && (c16.paired || !one_stage)) p = make_plan<T, 2, 4>(C, kV_2x4, c16.paired);
         else if (one_stage) p = make_plan<T, 1, 4, 1>(C, kV_1x4s1, 0);
         else p = make_plan<T, 1, 4>(C, kV_1x4, c8.paired);
@@ -1444,7 +1456,7 @@ Plan choose_plan(int C, int P, bool paged) {
     // 512 resident workgroups: heavy and light tiles side by side on each CU
     // (T=512 fp32 +7%, C=1024 P=0 bf16 +8%, P=1024 +3.5%); over several
     // rounds the heaviest-first order does better (T=1536 fp32: -6%).
-    const bool two_per_cu = sizeof(T) == 4 ? p.variant == kV_1x4s1 : p.variant != kV_8x2;
+    const bool two_per_cu = sizeof(T) == 4 ? (p.variant == kV_1x4s1 || p.variant == kV_2x4s1) : p.variant != kV_8x2;
     if (!p.paired && two_per_cu && p.grid <= 2 * 256) p.paired = 2;
     if (paged) p.lds += 4 * 2 * p.bk;   // the row offsets of two tiles
     return p;
@@ -1477,6 +1489,9 @@ hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, 
         case kV_1x4s1:   // planned for fp32 plain caches only
             if constexpr (MODE != kPlain || sizeof(T) != 4) return hipErrorInvalidValue;
             else return launch<T, 1, 4, MODE, 1>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
+        case kV_2x4s1:   // planned for fp32 plain caches only
+            if constexpr (MODE != kPlain || sizeof(T) != 4) return hipErrorInvalidValue;
+            else return launch<T, 2, 4, MODE, 1>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
         case kV_8x2:   // planned for bf16 only, never with key splits
             if constexpr ((MODE & kSplit) != 0 || sizeof(T) != 2) return hipErrorInvalidValue;
             else return launch<T, 8, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, clk, stream);

@@ -182,8 +182,9 @@ def test_fp32_plans_balance_causal_work():
     """Row-tile height and pairing per shape (see the planner's makespan
     estimate): (rows per item, workgroups, items per workgroup)."""
     want = {(2048, 2048): (32, 256, 2), (2048, 0): (32, 256, 2), (512, 15872): (16, 256, 1),
-            (1024, 0): (16, 256, 2), (1536, 0): (8, 1536, 1), (512, 0): (8, 512, 1), (600, 0): (16, 304, 1),
-            (255, 3): (8, 256, 1), (1000, 13): (16, 256, 2), (1500, 100): (8, 1504, 1), (2049, 7): (32, 520, 1),
+            (1024, 0): (16, 512, 1), (1536, 0): (8, 1536, 1), (512, 0): (8, 512, 1), (600, 0): (16, 304, 1),
+            (255, 3): (8, 256, 1), (1000, 13): (16, 504, 1), (1500, 100): (8, 1504, 1), (2049, 7): (32, 520, 1),
+            (1024, 16384): (32, 256, 1), (1100, 0): (16, 552, 1),
             (17, 31): (8, 24, 1), (768, 0): (16, 384, 1), (1530, 0): (8, 1536, 1)}
     for (C, P), w in want.items():
         p = cpf.plan(C, P)
@@ -191,16 +192,23 @@ def test_fp32_plans_balance_causal_work():
 
 
 def test_one_staging_buffer_only_where_its_items_fill_whole_rounds():
-    """The one-stage 8-row shape (64 KiB of LDS, two workgroups per CU: 512
-    slots) is planned for short-prefix plain chunks whose 8-row items fill
-    whole rounds of the slots, never for paged caches or long prefixes."""
-    ONE_STAGE = 7
+    """The one-stage shapes (64 KiB of LDS, two workgroups per CU: 512 slots)
+    are planned for plain chunks whose items fill whole rounds of the slots:
+    8-row items for short prefixes, 16-row items at C = 961..1024 with
+    P <= 4C; never for paged caches."""
+    ONE_STAGE, ONE_STAGE16 = 7, 8
     for C, P in [(512, 0), (1024 + 512, 0), (1530, 0), (1500, 100), (512, 128)]:
         p = cpf.plan(C, P)
         assert p["variant"] == ONE_STAGE and p["lds_bytes"] == 65536, (C, P, p)
         assert cpf.plan(C, P, paged=True)["variant"] != ONE_STAGE
     for C, P in [(768, 0), (1024, 0), (257, 0), (512, 15872), (512, 129), (2048, 0), (100, 0)]:
         assert cpf.plan(C, P)["variant"] != ONE_STAGE, (C, P)
+    for C, P in [(961, 0), (1000, 13), (1024, 0), (1024, 4096)]:
+        p = cpf.plan(C, P)
+        assert p["variant"] == ONE_STAGE16 and p["lds_bytes"] == 65536 and p["grid"] <= 512, (C, P, p)
+        assert cpf.plan(C, P, paged=True)["variant"] != ONE_STAGE16
+    for C, P in [(960, 0), (1025, 0), (1024, 4097), (768, 0)]:
+        assert cpf.plan(C, P)["variant"] != ONE_STAGE16, (C, P)
 
 
 def test_long_chunk_workgroup_shapes():
