@@ -291,10 +291,16 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     constexpr bool SPLIT = (MODE & kSplit) != 0;
 
     // One LDS object: K/V stages (reused by the key-split merge), then, for a
-    // paged cache, the row offsets of two tiles.  A second __shared__ array
-    // would make the compiler wait for every HBM->LDS load in flight before
-    // each LDS read of the staged tiles.
-    __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[G::kLdsBytes + (PAGED ? 2 * kBK * 4 : 0)];
+    // paged cache, the row offsets of two tiles, then (fp32, where it fits)
+    // the Q rows of one work item.  A second __shared__ array would make the
+    // compiler wait for every HBM->LDS load in flight before each LDS read of
+    // the staged tiles.
+    constexpr int kQOff = G::kLdsBytes + (PAGED ? 2 * kBK * 4 : 0);
+    constexpr int kQRowBytes = kGroup * kD * 4;                   // the group's 4 heads of one fp32 row
+    constexpr int kQBytes = kRows * kQRowBytes;
+    constexpr bool kQLds = kF32 && kQOff + kQBytes <= (ST == 2 ? 163840 : 81920);
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[kQOff + (kQLds ? kQBytes : 0)];
+    unsigned char* const qbuf = lds_raw + kQOff;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -385,6 +391,30 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     : kNoRow;
         }
     };
+    // fp32 Q through LDS: the rows of work item i0q go from memory straight
+    // into LDS (one 1 KiB row per load instruction: the group's 4 heads), once
+    // for the workgroup instead of once per key-split wave, and each wave reads
+    // its 8 rows from there.  Position p of a row holds logical chunk
+    // p ^ ((4 * (row % 4) + head) % 16) (the head being p / 16, which the XOR
+    // keeps), so the 16 lanes of an LDS cycle (4 rows x 4 heads at one chunk)
+    // read 16 different bank groups.
+    auto issue_q = [&](int i0q) {
+        const int rows_q = min(kRows, C - i0q);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(q + (size_t)i0q * kHQ * kD), (short)0, (uint32_t)rows_q * kHQ * kD * 4, 0x00020000);
+        int L = lane;
+        asm volatile("" : "+v"(L));
+#pragma unroll
+        for (int u = 0; u < (kRows + G::kWaves - 1) / G::kWaves; ++u) {
+            const int r = wid + u * G::kWaves;      // item row of this instruction; past the chunk it reads zero
+            if (kRows % G::kWaves != 0 && r >= kRows) break;
+            const int lc = L ^ ((4 * (r & 3) + (L >> 4)) & 15);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)(qbuf + r * kQRowBytes), 16,
+                                                     (uint32_t)((r * kHQ + g * kGroup) * kD * 4 + lc * 16), 0, 0, 0);
+        }
+    };
+    bool q_staged = false;     // qbuf already holds the next work item's Q
+
     auto issue_tile = [&](int t, int stage) {
         const int key0 = kb + t * kBK;
         uint32_t range;
@@ -450,6 +480,10 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             if (ntiles > 1) store_offset(1, e1);
             __syncthreads();
         }
+        if constexpr (kQLds) {
+            if (!q_staged) issue_q(i0);
+            q_staged = false;
+        }
         issue_tile(0, 0);
 
         // ---- Q operand (B of S^T = K Q^T), held for the whole key loop ----
@@ -471,7 +505,9 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         {
             const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(q + (size_t)i0 * kHQ * kD), (short)0, (uint32_t)item_rows * kHQ * kD * sizeof(T), 0x00020000);
-            if constexpr (kF32) {
+            if constexpr (kQLds) {
+                (void)rq;                           // read from LDS once the item's first tile is in
+            } else if constexpr (kF32) {
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
                     const f4 x = __builtin_bit_cast(
@@ -708,9 +744,37 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // ---- key loop over staged tiles (double-buffered, unrolled by two) ----
         // Tile t+1's loads go to the other stage while tile t is consumed; that
         // stage was last read before the previous barrier.
-        __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile 0 has landed in LDS
+        __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): tile 0 (and Q) have landed in LDS
         __syncthreads();
         if (it < 2) mark(it == 0 ? 4 : 7);       // the item's first tile is in LDS
+        if constexpr (kQLds) {
+            // qf[s] = q[row][head][32*hh + s] * log2(e)/8 from this wave's rows of qbuf
+            int lane3 = lane;
+            asm volatile("" : "+v"(lane3));
+            const int qr = 8 * wr + ((lane3 & 31) >> 2);   // row within the item
+            const int qh = lane3 & 3;
+            const int qhh = lane3 >> 5;
+            const unsigned char* qrow = qbuf + qr * kQRowBytes;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int pos = (qh * 16 + qhh * 8 + c) ^ ((4 * (qr & 3) + qh) & 15);
+                const f4 x = *reinterpret_cast<const f4*>(qrow + pos * 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qf[4 * c + e] = x[e] * kScaleLog2;
+            }
+        }
+        // The next work item's Q goes into qbuf once every wave has read this
+        // one's, i.e. after the barrier that ends tile 0; it lands with tile 1.
+        auto stage_next_q = [&](int t) {
+            if constexpr (kQLds && ST == 2) {      // one-stage plans have one item per workgroup
+                if (t == 0 && it + 1 < nitems) {
+                    issue_q(items[it + 1] * kRows);
+                    q_staged = true;
+                }
+            } else {
+                (void)t;
+            }
+        };
         // One staging buffer: every tile is consumed, then the next is loaded
         // into the same buffer; the other workgroup on the CU computes meanwhile.
         if constexpr (ST == 1) {
@@ -720,6 +784,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                 __syncthreads();                      // every wave is done with the tile
                 if (t + 1 < ntiles) {
                     issue_tile(t + 1, 0);
+                    stage_next_q(t);
                     __builtin_amdgcn_s_waitcnt(0x3f70);
                     __syncthreads();
                 }
@@ -744,6 +809,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
             if (t + 1 < ntiles) {
                 vo = prefetch_v(std::integral_constant<int, 1>{}, t + 1);
                 if (t + 2 < ntiles) issue_tile(t + 2, 0);
+                stage_next_q(t);
                 if constexpr (PAGED) {
                     if (t + 3 < ntiles) ent = fetch_entry(t + 3);
                 }
@@ -762,6 +828,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         int lane2 = lane;
         asm volatile("" : "+v"(lane2));
         const uint32_t out_vec = (uint32_t)((8 * wr + ((lane2 & 31) >> 2)) * kHQ + g * kGroup + (lane2 & 3)) * kD;
+        const int hh2 = lane2 >> 5;              // the half-wave, from the same copy
 
         // ---- merge key splits (log-sum-exp), in LDS ----
         if constexpr (KS > 1) {
@@ -813,16 +880,16 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                 // rows 8a+4hh+j: dims 16a+8hh+2j (o0), +1 (o1)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    st4(8 * hh + 16 * a, f4{o0[4 * a] * sc, o1[4 * a] * sc, o0[4 * a + 1] * sc, o1[4 * a + 1] * sc});
-                    st4(8 * hh + 16 * a + 4,
+                    st4(8 * hh2 + 16 * a, f4{o0[4 * a] * sc, o1[4 * a] * sc, o0[4 * a + 1] * sc, o1[4 * a + 1] * sc});
+                    st4(8 * hh2 + 16 * a + 4,
                         f4{o0[4 * a + 2] * sc, o1[4 * a + 2] * sc, o0[4 * a + 3] * sc, o1[4 * a + 3] * sc});
                 }
             } else {
                 // rows 8a+4hh+j: dims 8a+4hh+j (o0), +32 (o1)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    st4(4 * hh + 8 * a, f4{o0[4 * a] * sc, o0[4 * a + 1] * sc, o0[4 * a + 2] * sc, o0[4 * a + 3] * sc});
-                    st4(4 * hh + 32 + 8 * a,
+                    st4(4 * hh2 + 8 * a, f4{o0[4 * a] * sc, o0[4 * a + 1] * sc, o0[4 * a + 2] * sc, o0[4 * a + 3] * sc});
+                    st4(4 * hh2 + 32 + 8 * a,
                         f4{o1[4 * a] * sc, o1[4 * a + 1] * sc, o1[4 * a + 2] * sc, o1[4 * a + 3] * sc});
                 }
             }
