@@ -144,6 +144,20 @@ struct Geo {
     // Merge buffer for key splits: per (row-wave, split>0) wave, 34 floats/lane.
     static constexpr int kMergeBytes = KS > 1 ? NW * (KS - 1) * 34 * 64 * 4 : 0;
     static constexpr int kLdsBytes = ST * kStageBytes > kMergeBytes ? ST * kStageBytes : kMergeBytes;
+    // Paged cache: the row offsets of two tiles follow the tiles.  fp32: a work
+    // item's Q rows (the group's 4 heads, 1 KiB per row) are staged in LDS,
+    // after the tiles where they fit in the 160 KiB of a workgroup (half that
+    // when two one-stage workgroups share a CU), else in the second stage's V
+    // tile, which is free until the item's second tile is issued.
+    static constexpr int kQRowBytes = kGroup * kD * 4;
+    static constexpr int kQBytes = kRows * kQRowBytes;
+    static constexpr int kLdsLimit = ST == 2 ? 163840 : 81920;
+    static constexpr int q_offset(bool paged) { return kLdsBytes + (paged ? 2 * kBK * 4 : 0); }
+    static constexpr bool q_after(bool paged) { return sizeof(T) == 4 && q_offset(paged) + kQBytes <= kLdsLimit; }
+    static constexpr bool q_in_stage1(bool paged) {
+        return sizeof(T) == 4 && !q_after(paged) && ST == 2 && kQBytes <= kTileBytes;
+    }
+    static constexpr int lds_total(bool paged) { return q_offset(paged) + (q_after(paged) ? kQBytes : 0); }
 };
 
 // Row-dependent chunk permutations (XOR codes) of staged rows.  A 16-byte
@@ -295,12 +309,12 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
     // the Q rows of one work item.  A second __shared__ array would make the
     // compiler wait for every HBM->LDS load in flight before each LDS read of
     // the staged tiles.
-    constexpr int kQOff = G::kLdsBytes + (PAGED ? 2 * kBK * 4 : 0);
-    constexpr int kQRowBytes = kGroup * kD * 4;                   // the group's 4 heads of one fp32 row
-    constexpr int kQBytes = kRows * kQRowBytes;
-    constexpr bool kQLds = kF32 && kQOff + kQBytes <= (ST == 2 ? 163840 : 81920);
-    __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[kQOff + (kQLds ? kQBytes : 0)];
-    unsigned char* const qbuf = lds_raw + kQOff;
+    constexpr int kQRowBytes = G::kQRowBytes;
+    constexpr bool kQAfter = G::q_after(PAGED);          // Q rows after the tiles (and row offsets)
+    constexpr bool kQInStage1 = G::q_in_stage1(PAGED);   // else in the second stage's V tile
+    constexpr bool kQLds = kQAfter || kQInStage1;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[G::lds_total(PAGED)];
+    unsigned char* const qbuf = lds_raw + (kQInStage1 ? G::kTileBytes : G::q_offset(PAGED));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -766,7 +780,7 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // The next work item's Q goes into qbuf once every wave has read this
         // one's, i.e. after the barrier that ends tile 0; it lands with tile 1.
         auto stage_next_q = [&](int t) {
-            if constexpr (kQLds && ST == 2) {      // one-stage plans have one item per workgroup
+            if constexpr (kQAfter && ST == 2) {    // one-stage plans have one item per workgroup
                 if (t == 0 && it + 1 < nitems) {
                     issue_q(items[it + 1] * kRows);
                     q_staged = true;
@@ -795,6 +809,9 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // (every wave issued those before the previous barrier).
         for (int t = 0; ST == 2 && t < ntiles; t += 2) {
             VOps vo = prefetch_v(std::integral_constant<int, 0>{}, t);
+            if constexpr (kQInStage1) {
+                if (t == 0) __syncthreads();          // every wave has read its Q out of the second stage
+            }
             if (t + 1 < ntiles) issue_tile(t + 1, 1);
             int ent = 0;
             if constexpr (PAGED) {
@@ -1429,14 +1446,14 @@ struct Plan {
 // pair < 0: pair tiles i and n-1-i when that still leaves a workgroup per CU;
 // otherwise pair iff pair != 0.
 template <typename T, int NW, int KS, int ST = 2>
-Plan make_plan(int C, int variant, int pair = -1) {
+Plan make_plan(int C, int variant, int pair = -1, bool paged = false) {
     using G = Geo<T, NW, KS, ST>;
     Plan p{};
     p.rows = G::kRows;
     p.ks = KS;
     p.threads = G::kThreads;
     p.bk = G::kBK;
-    p.lds = G::kLdsBytes;
+    p.lds = G::lds_total(paged);
     p.variant = variant;
     p.n_row_tiles = (C + G::kRows - 1) / G::kRows;
     const int pairs = (p.n_row_tiles + 1) / 2;
@@ -1506,17 +1523,18 @@ Plan choose_plan(int C, int P, bool paged) {
         // paired two-stage 16-row items at P = 0..4096; -2% at P = 16384)
         const bool one_stage16 = !paged && C > 960 && C <= 1024 && P <= 4 * C;
         if (one_stage16) p = make_plan<T, 2, 4, 1>(C, kV_2x4s1, 0);
-        else if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired);
-        else if (c16.t <= c8.t && (c16.paired || !one_stage)) p = make_plan<T, 2, 4>(C, kV_2x4, c16.paired);
+        else if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired, paged);
+        else if (c16.t <= c8.t && (c16.paired || !one_stage)) p = make_plan<T, 2, 4>(C, kV_2x4, c16.paired, paged);
         else if (one_stage) p = make_plan<T, 1, 4, 1>(C, kV_1x4s1, 0);
-        else p = make_plan<T, 1, 4>(C, kV_1x4, c8.paired);
+        else p = make_plan<T, 1, 4>(C, kV_1x4, c8.paired, paged);
     } else {
         // two 16-row workgroups fit a CU, so pairing them into 256 workgroups
         // would leave half the slots empty: they stay unpaired
-        p = C >= 2048 ? (C >= 4096 ? make_plan<T, 8, 2>(C, kV_8x2, shape_cost(C, P, 64, 1.0, 64.0 * 177.0).paired)
-                                             : make_plan<T, 4, 2>(C, kV_4x2))
-            : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4, 0)
-                       : make_plan<T, 1, 4>(C, kV_1x4);
+        p = C >= 2048 ? (C >= 4096 ? make_plan<T, 8, 2>(C, kV_8x2, shape_cost(C, P, 64, 1.0, 64.0 * 177.0).paired,
+                                                            paged)
+                                             : make_plan<T, 4, 2>(C, kV_4x2, -1, paged))
+            : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4, 0, paged)
+                       : make_plan<T, 1, 4>(C, kV_1x4, -1, paged);
     }
     // Unpaired plans that run two workgroups per CU (fp32 with one staging
     // buffer, every bf16 shape but the 64-row one) and fit in one round of
@@ -1525,7 +1543,6 @@ Plan choose_plan(int C, int P, bool paged) {
     // rounds the heaviest-first order does better (T=1536 fp32: -6%).
     const bool two_per_cu = sizeof(T) == 4 ? (p.variant == kV_1x4s1 || p.variant == kV_2x4s1) : p.variant != kV_8x2;
     if (!p.paired && two_per_cu && p.grid <= 2 * 256) p.paired = 2;
-    if (paged) p.lds += 4 * 2 * p.bk;   // the row offsets of two tiles
     return p;
 }
 

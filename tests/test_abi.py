@@ -192,20 +192,21 @@ def test_fp32_plans_balance_causal_work():
 
 
 def test_one_staging_buffer_only_where_its_items_fill_whole_rounds():
-    """The one-stage shapes (64 KiB of LDS, two workgroups per CU: 512 slots)
+    """The one-stage shapes (64 KiB of K/V tiles and 1 KiB per Q row of LDS,
+    two workgroups per CU: 512 slots)
     are planned for plain chunks whose items fill whole rounds of the slots:
     8-row items for short prefixes, 16-row items at C = 961..1024 with
     P <= 4C; never for paged caches."""
     ONE_STAGE, ONE_STAGE16 = 7, 8
     for C, P in [(512, 0), (1024 + 512, 0), (1530, 0), (1500, 100), (512, 128)]:
         p = cpf.plan(C, P)
-        assert p["variant"] == ONE_STAGE and p["lds_bytes"] == 65536, (C, P, p)
+        assert p["variant"] == ONE_STAGE and p["lds_bytes"] == 65536 + 1024 * 8, (C, P, p)
         assert cpf.plan(C, P, paged=True)["variant"] != ONE_STAGE
     for C, P in [(768, 0), (1024, 0), (257, 0), (512, 15872), (512, 129), (2048, 0), (100, 0)]:
         assert cpf.plan(C, P)["variant"] != ONE_STAGE, (C, P)
     for C, P in [(961, 0), (1000, 13), (1024, 0), (1024, 4096)]:
         p = cpf.plan(C, P)
-        assert p["variant"] == ONE_STAGE16 and p["lds_bytes"] == 65536 and p["grid"] <= 512, (C, P, p)
+        assert p["variant"] == ONE_STAGE16 and p["lds_bytes"] == 65536 + 1024 * 16 and p["grid"] <= 512, (C, P, p)
         assert cpf.plan(C, P, paged=True)["variant"] != ONE_STAGE16
     for C, P in [(960, 0), (1025, 0), (1024, 4097), (768, 0)]:
         assert cpf.plan(C, P)["variant"] != ONE_STAGE16, (C, P)

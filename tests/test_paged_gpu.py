@@ -95,7 +95,11 @@ def test_paged_equals_contiguous_bitwise(C, P, dtype):
     kp, vp, table = synth.to_pages(k, v, 16, 5401 + C)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     pp, pc = cpf.plan(C, P, tdt, paged=True), cpf.plan(C, P, tdt)
-    assert pp.pop("lds_bytes") == pc.pop("lds_bytes") + 2 * 4 * pc["keys_per_tile"]   # + row offsets of two tiles
+    lp, lc = pp.pop("lds_bytes"), pc.pop("lds_bytes")
+    offsets = 2 * 4 * pc["keys_per_tile"]                  # the row offsets of two tiles
+    qrows = 1024 * pc["rows_per_item"] if dtype == "f32" else 0
+    # fp32 Q rows that no longer fit after the offsets move into a staging tile
+    assert lp == lc + offsets or (lc + offsets > 160 * 1024 and lp == lc - qrows + offsets), (lp, lc)
     assert pp == pc
     paged = run_paged(q, kp, vp, table, P, dtype)
     contig = cpf.attn_prefill(to_gpu(q, dtype), to_gpu(k, dtype), to_gpu(v, dtype), P=P).cpu().numpy()
