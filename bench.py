@@ -109,8 +109,9 @@ def clock_from_log(clocks):
             "max_mhz": round(float(mhz[-1]), 1), "busy_average_mhz": round(float(cyc.sum() / tick.sum() * 100.0), 1),
             "workgroups": int(len(mhz)), "phases_us": phases,
             "source": "attn_prefill_clocked (the same kernels): each workgroup's shader-clock counter over the fixed "
-                      "100 MHz counter from its start to its end, on the last of 10 calls run back to back right "
-                      "after the timed steps; phases are the medians over workgroups of the spans between its marks"}
+                      "100 MHz counter from its start to its end, on the middle one of the timed steps (that step "
+                      "goes through attn_prefill_clocked, the same kernel logging into a buffer allocated beforehand); "
+                      "phases are the medians over workgroups of the spans between its marks"}
 
 
 def kernel_source_hash() -> str:
@@ -549,26 +550,30 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: K steps, synchronised on both sides; HIP events on the
-    # stream the kernel is launched on give the per-launch device time; the
-    # clock the kernels run at is logged by the same kernels afterwards
+    # stream the kernel is launched on give the per-launch device time.  The
+    # middle step (plain caches) goes through attn_prefill_clocked: the same
+    # kernel, which then also logs its clock into a buffer allocated before
+    # the region, so the clock is the one the timed steps ran at
+    logged = not args.no_clock and not paged and not splitkv
+    if logged:
+        plan_grid = cpf.plan(C, P, torch.float32 if dt == "f32" else torch.bfloat16)["grid"]
+        clk_buf = torch.zeros((max(plan_grid, 1), cpf.CLOCK_WORDS), dtype=torch.int64, device=dev)
+    mid = args.steps // 2
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        call()
+    for i in range(args.steps):
+        if logged and i == mid:
+            cpf.attn_prefill_clocked(qd, kd, vd, out=out, P=P, stream=stream, clocks=clk_buf)
+        else:
+            call()
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    # the clock the kernels run at, logged by the same kernels (plain caches)
-    clock = None
-    if not args.no_clock and not paged and not splitkv:
-        for _ in range(10):
-            _, clk_log = cpf.attn_prefill_clocked(qd, kd, vd, out=out, P=P, stream=stream)
-        torch.cuda.synchronize()
-        clock = clock_from_log(clk_log)
+    clock = clock_from_log(clk_buf[:plan_grid]) if logged else None
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 

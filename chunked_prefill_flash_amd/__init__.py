@@ -215,7 +215,8 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
 
 
 def attn_prefill_clocked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
-                         P: int | None = None, stream: torch.cuda.Stream | None = None):
+                         P: int | None = None, stream: torch.cuda.Stream | None = None,
+                         clocks: torch.Tensor | None = None):
     """attn_prefill that also logs the clock: returns (out, clocks) with
     clocks an int64 [workgroups][CLOCK_WORDS] device tensor (not yet
     synchronised, zero where a mark was not written): (shader clock, 100 MHz
@@ -223,14 +224,21 @@ def attn_prefill_clocked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out:
     clock when its first work item's first tile is in LDS [4], when that
     item's key loop is done [5] and its output stored [6], and when a second
     item's first tile is in LDS [7].  A workgroup's clock in MHz is
-    (c[:, 2] - c[:, 0]) / (c[:, 3] - c[:, 1]) * 100."""
+    (c[:, 2] - c[:, 0]) / (c[:, 3] - c[:, 1]) * 100.  `clocks` may be given:
+    a contiguous int64 device tensor of at least that many rows, written in
+    place with nothing allocated or cleared (a mark not written keeps its old
+    value), so that a timed loop can log one of its calls."""
     C = q.shape[0]
     if P is None:
         P = k.shape[0] - C
     grid = plan(C, P, q.dtype)["grid"] if C > 0 else 0
     s = _stream(stream, q.device)
-    with torch.cuda.stream(s):
-        clocks = torch.zeros((max(grid, 1), CLOCK_WORDS), dtype=torch.int64, device=q.device)
+    if clocks is None:
+        with torch.cuda.stream(s):
+            clocks = torch.zeros((max(grid, 1), CLOCK_WORDS), dtype=torch.int64, device=q.device)
+    elif (clocks.dtype != torch.int64 or clocks.device != q.device or not clocks.is_contiguous()
+          or clocks.dim() != 2 or clocks.shape[1] != CLOCK_WORDS or clocks.shape[0] < grid):
+        raise ValueError("clocks must be a contiguous int64 [>= %d][%d] tensor on %s" % (grid, CLOCK_WORDS, q.device))
     if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype in %s" % list(DTYPES))
     if q.dim() != 3 or q.shape[1:] != (HQ, D) or k.shape != (P + C, HKV, D) or v.shape != k.shape:

@@ -54,3 +54,27 @@ def test_clocked_rejects_a_short_clock_buffer():
     assert lib.attn_prefill_clocked(*args, buf.data_ptr() + 4, n, None) == 4
     assert lib.attn_prefill_clocked(*args, out.data_ptr(), n, None) == 6
     torch.cuda.synchronize()
+
+
+def test_clocked_writes_a_given_buffer_in_place():
+    """The form the benchmark times: a clock buffer allocated beforehand is
+    written in place (nothing allocated or cleared by the call), rows past the
+    launch's workgroups are left alone, and the output is attn_prefill's."""
+    C, P = 300, 1000
+    q, k, v = synth.case_plain(C, P, 9700)
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    grid = cpf.plan(C, P)["grid"]
+    buf = torch.full((grid + 3, cpf.CLOCK_WORDS), -1, dtype=torch.int64, device="cuda")
+    want = cpf.attn_prefill(qd, kd, vd, P=P)
+    for _ in range(2):
+        got, clocks = cpf.attn_prefill_clocked(qd, kd, vd, P=P, clocks=buf)
+        torch.cuda.synchronize()
+        assert clocks.data_ptr() == buf.data_ptr() and clocks.shape == (grid, cpf.CLOCK_WORDS)
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+        c = buf.cpu().numpy()
+        assert np.all(c[grid:] == -1)
+        assert np.all(c[:grid, 2] > c[:grid, 0]) and np.all(c[:grid, 3] > c[:grid, 1])
+    with pytest.raises(ValueError):
+        cpf.attn_prefill_clocked(qd, kd, vd, P=P, clocks=buf[:grid - 1])
+    with pytest.raises(ValueError):
+        cpf.attn_prefill_clocked(qd, kd, vd, P=P, clocks=buf.to(torch.int32))
