@@ -69,3 +69,39 @@ def test_rocprof_summary_scales_traffic_by_the_copy_calibration(tmp_path):
     assert e["kernel_source_sha256_16"] == bench.kernel_source_hash()
     text = open(out / "attn_prefill_c2048_p2048_f32_counters.md").read()
     assert "rocprofv3 --pmc FETCH_SIZE" in text and "ratio" in text
+
+
+def test_clock_from_log_on_a_synthetic_log():
+    """The benchmark's reading of the clock log, on a hand-made one: two
+    workgroups at exactly 2000 and 2400 MHz (shader-clock cycles over 100 MHz
+    ticks), the second with a second work item; medians, busy-time average,
+    phase spans in microseconds at each workgroup's own clock, kernel span
+    and start spread from the 100 MHz counter."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import numpy as np
+    import torch
+
+    def wg(mhz, t0_tick, ticks, marks_us, second_us=None):
+        cyc_per_us = mhz                       # cycles per microsecond at `mhz` MHz
+        c0 = 1_000_000
+        row = [c0, t0_tick, c0 + int(ticks / 100.0 * cyc_per_us), t0_tick + ticks]
+        row += [c0 + int(u * cyc_per_us) for u in marks_us]
+        row += [0 if second_us is None else c0 + int(second_us * cyc_per_us)]
+        return row
+
+    log = torch.tensor([wg(2000.0, 500, 1000, [1.0, 6.0, 7.0]),                  # 10 us at 2000 MHz
+                        wg(2400.0, 520, 2000, [2.0, 8.0, 9.0], second_us=10.0)],  # 20 us at 2400 MHz
+                       dtype=torch.int64)
+    c = bench.clock_from_log(log)
+    assert c["median_mhz"] == 2400.0 and c["min_mhz"] == 2000.0 and c["max_mhz"] == 2400.0
+    # busy-time average: all cycles over all ticks = (20000 + 48000) / 3000 ticks * 100
+    assert abs(c["busy_average_mhz"] - (20000 + 48000) / 3000 * 100) < 0.2
+    ph = c["phases_us"]
+    assert ph["workgroups_with_two_items"] == 1
+    assert ph["first_item_prologue"] == 1.5 and ph["first_item_key_loop"] == 5.5
+    assert ph["first_item_epilogue"] == 1.0
+    assert ph["second_item_prologue"] == 1.0 and ph["second_item_rest"] == 10.0
+    assert ph["workgroup"] == 15.0
+    assert ph["kernel_span"] == round((2520 - 500) / 100.0, 2) and ph["start_spread"] == 0.2
+    assert np.isfinite(list(v for v in ph.values() if v is not None)).all()
