@@ -890,15 +890,8 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         auto store_o = [&](float* item, float sc) {
             const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)item, (short)0, (uint32_t)item_rows * kHQ * kD * 4, 0x00020000);
-            // One-stage plans (short prompts, two workgroups per CU) store the
-            // output non-temporally: T=512 and T=1024 about 2% faster.  The
-            // two-stage plans keep the default policy, under which they were
-            // faster (T=2048 by 1%, bf16 C=2048 P=500 by 7%), and so do key-split
-            // partials, which the merge kernel reads next.
-            constexpr int kPolicy = ST == 1 && !SPLIT ? 2 : 0;   // 2: nt
             auto st4 = [&](uint32_t elem, f4 x) {
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro, (out_vec + elem) * 4, 0,
-                                                       kPolicy);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro, (out_vec + elem) * 4, 0, 0);
             };
             if constexpr (kF32) {
                 // rows 8a+4hh+j: dims 16a+8hh+2j (o0), +1 (o1)
