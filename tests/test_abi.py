@@ -215,7 +215,8 @@ def test_one_staging_buffer_only_where_its_items_fill_whole_rounds():
 def test_long_chunk_workgroup_shapes():
     for paged in (False, True):
         assert cpf.plan(2048, 2048, paged=paged)["threads"] == 1024          # fp32: 32 rows, 16 waves
-        assert cpf.plan(2048, 2048, dtype=torch.bfloat16, paged=paged)["threads"] == 512
+        bf = cpf.plan(2048, 2048, dtype=torch.bfloat16, paged=paged)            # bf16: 32 rows, unpaired,
+        assert (bf["threads"], bf["grid"], bf["items_per_workgroup"]) == (512, 512, 1)   # two per CU
     for paged in (False, True):                                             # bf16: 64 rows, paired
         bf = cpf.plan(4096, 28672, dtype=torch.bfloat16, paged=paged)
         assert (bf["rows_per_item"], bf["threads"], bf["grid"], bf["items_per_workgroup"]) == (64, 1024, 256, 2)
