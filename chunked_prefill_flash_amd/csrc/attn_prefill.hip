@@ -1509,23 +1509,28 @@ Plan choose_plan(int C, int P, bool paged) {
                         c8 = shape_cost(C, P, 8, 0.68, kItem);
         // One staging buffer with 8-row items, unpaired: two workgroups share a
         // CU (512 slots), each nearly as fast as alone since the other computes
-        // while it waits on its loads.  Measured against the two-stage 8-row
-        // and unpaired 16-row plans it wins when its items fill whole rounds
-        // of the 512 slots (T=512 +16%; T=1536 and C=1500 P=100 +4%) and loses
-        // where the last round is partial (T=768 -11%) and to paired 16-row
-        // items (T=1024 -10%) and on long prefixes (C=512 P=15872 -3%); plain
-        // caches and short prefixes (P <= C/4) only.
-        const int rem = (8 * ((C + 7) / 8)) % 512;
-        const bool one_stage = !paged && P <= C / 4 && (rem == 0 || rem >= 440);
+        // while it waits on its loads.  Measured against the two-stage plans
+        // it wins where its workgroups (one per 8 rows and KV group) fill one
+        // round of the 512 slots or whole rounds (T=512 +16%; T=1536, C=1500
+        // P=100 +4%; C=384 P=1000 +22%; C=1536 P=1536 +10%) or where a long
+        // prefix makes the items alike so a partial round costs little (C=768
+        // P=2000 +17%); it loses with a partial round of causal items (T=768
+        // -11%), to the 32-row pairs from 2048 rows (-4 to -7%) and on
+        // prefixes past 8C (C=512 P=15872 -3%, C=1024 P=16000 -4%).  Plain
+        // caches only.
+        const int wgs = 8 * ((C + 7) / 8);
+        const int rem = wgs % 512;
+        const bool one_stage =
+            !paged && C < 2048 && P <= 8 * C && (wgs <= 512 || rem == 0 || rem >= 440 || P >= C);
         // 16-row items with one staging buffer, two workgroups per CU (four
         // waves per SIMD instead of the two of a 16-row workgroup alone), where
         // they fill the 512 slots in one round: C = 961..1024 (+4-9% over the
         // paired two-stage 16-row items at P = 0..4096; -2% at P = 16384)
         const bool one_stage16 = !paged && C > 960 && C <= 1024 && P <= 4 * C;
         if (one_stage16) p = make_plan<T, 2, 4, 1>(C, kV_2x4s1, 0);
-        else if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired, paged);
-        else if (c16.t <= c8.t && (c16.paired || !one_stage)) p = make_plan<T, 2, 4>(C, kV_2x4, c16.paired, paged);
         else if (one_stage) p = make_plan<T, 1, 4, 1>(C, kV_1x4s1, 0);
+        else if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired, paged);
+        else if (c16.t <= c8.t) p = make_plan<T, 2, 4>(C, kV_2x4, c16.paired, paged);
         else p = make_plan<T, 1, 4>(C, kV_1x4, c8.paired, paged);
     } else {
         // two (4,2) or (2,4) workgroups fit a CU, so pairing their items into

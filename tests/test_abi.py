@@ -185,7 +185,8 @@ def test_fp32_plans_balance_causal_work():
             (1024, 0): (16, 512, 1), (1536, 0): (8, 1536, 1), (512, 0): (8, 512, 1), (600, 0): (16, 304, 1),
             (255, 3): (8, 256, 1), (1000, 13): (16, 504, 1), (1500, 100): (8, 1504, 1), (2049, 7): (32, 520, 1),
             (1024, 16384): (32, 256, 1), (1100, 0): (16, 552, 1),
-            (17, 31): (8, 24, 1), (768, 0): (16, 384, 1), (1530, 0): (8, 1536, 1)}
+            (17, 31): (8, 24, 1), (768, 0): (16, 384, 1), (1530, 0): (8, 1536, 1), (768, 2000): (8, 768, 1),
+            (1100, 4400): (8, 1104, 1), (300, 3000): (8, 304, 1)}
     for (C, P), w in want.items():
         p = cpf.plan(C, P)
         assert (p["rows_per_item"], p["grid"], p["items_per_workgroup"]) == w, (C, P, p)
@@ -193,16 +194,19 @@ def test_fp32_plans_balance_causal_work():
 
 def test_one_staging_buffer_only_where_its_items_fill_whole_rounds():
     """The one-stage shapes (64 KiB of K/V tiles and 1 KiB per Q row of LDS,
-    two workgroups per CU: 512 slots)
-    are planned for plain chunks whose items fill whole rounds of the slots:
-    8-row items for short prefixes, 16-row items at C = 961..1024 with
+    two workgroups per CU: 512 slots) are planned for plain chunks: 8-row
+    items below 2048 rows with P <= 8C whose workgroups (one per 8 rows and
+    KV group) fill one round or whole rounds of the slots, or whose prefix
+    (P >= C) makes the items alike; 16-row items at C = 961..1024 with
     P <= 4C; never for paged caches."""
     ONE_STAGE, ONE_STAGE16 = 7, 8
-    for C, P in [(512, 0), (1024 + 512, 0), (1530, 0), (1500, 100), (512, 128)]:
+    for C, P in [(512, 0), (1024 + 512, 0), (1530, 0), (1500, 100), (512, 128), (512, 129), (257, 0),
+                 (100, 0), (384, 1000), (768, 2000), (1536, 1536), (1100, 8800)]:
         p = cpf.plan(C, P)
         assert p["variant"] == ONE_STAGE and p["lds_bytes"] == 65536 + 1024 * 8, (C, P, p)
         assert cpf.plan(C, P, paged=True)["variant"] != ONE_STAGE
-    for C, P in [(768, 0), (1024, 0), (257, 0), (512, 15872), (512, 129), (2048, 0), (100, 0)]:
+    for C, P in [(768, 0), (896, 0), (1024, 0), (512, 15872), (1024, 16000), (1100, 8801), (2048, 0),
+                 (2048, 2048), (1792, 1000)]:
         assert cpf.plan(C, P)["variant"] != ONE_STAGE, (C, P)
     for C, P in [(961, 0), (1000, 13), (1024, 0), (1024, 4096)]:
         p = cpf.plan(C, P)

@@ -189,8 +189,9 @@ def test_edge_grid(C, P, dtype):
             assert np.all(got[p - P, 0] == np.float32(4.0))
 
 
-@pytest.mark.parametrize("C,P", [(255, 3), (256, 700), (600, 0), (1000, 13), (1024, 1), (1500, 100),
-                                 (2049, 7), (2100, 0), (1530, 0), (512, 128), (961, 2500), (1100, 0)])
+@pytest.mark.parametrize("C,P", [(255, 3), (256, 700), (300, 3000), (600, 0), (1000, 13), (1024, 1),
+                                 (1500, 100), (2049, 7), (2100, 0), (2048, 500), (1530, 0), (512, 128),
+                                 (961, 2500), (1100, 0), (768, 2000)])
 def test_every_launch_variant(C, P):
     """Covers the fp32 work items of 8, 16 and 32 rows, paired and unpaired
     row tiles, one and two staging buffers (16-row items with one buffer at
