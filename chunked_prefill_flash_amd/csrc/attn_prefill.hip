@@ -1511,22 +1511,28 @@ Plan choose_plan(int C, int P, bool paged) {
         // CU (512 slots), each nearly as fast as alone since the other computes
         // while it waits on its loads.  Measured against the two-stage plans
         // it wins where its workgroups (one per 8 rows and KV group) fill one
-        // round of the 512 slots or whole rounds (T=512 +16%; T=1536, C=1500
-        // P=100 +4%; C=384 P=1000 +22%; C=1536 P=1536 +10%) or where a long
+        // round of the 512 slots, whole rounds, or more than two rounds and
+        // most of a third (T=512 +16%; T=1536, C=1500 P=100 +4%; C=384 P=1000
+        // +22%; C=1536 P=1536 +10%; T=960, 1.9 rounds: -10%) or where a long
         // prefix makes the items alike so a partial round costs little (C=768
-        // P=2000 +17%); it loses with a partial round of causal items (T=768
-        // -11%), to the 32-row pairs from 2048 rows (-4 to -7%) and on
-        // prefixes past 8C (C=512 P=15872 -3%, C=1024 P=16000 -4%).  Plain
-        // caches only.
+        // P=2000 +17%, C=1100 P=12000 +31%: there the 32-row items take two
+        // rounds of 256 workgroups for 280).  It loses with a partial round of
+        // causal items (T=768 -11%), near 2048 rows to the 32-row items (C=1900
+        // to 2000: -4 to -7%) and on prefixes past 8C where 16- or 32-row
+        // items fill exactly the 256 CUs (C=512 P=15872 -3%, C=1024 P=16000
+        // -4%).  Plain caches only.
         const int wgs = 8 * ((C + 7) / 8);
         const int rem = wgs % 512;
-        const bool one_stage =
-            !paged && C < 2048 && P <= 8 * C && (wgs <= 512 || rem == 0 || rem >= 440 || P >= C);
+        const bool exact_fit = 8 * ((C + 31) / 32) == 256 || 8 * ((C + 15) / 16) == 256;
+        const bool one_stage = !paged && C < 1800 && !(P > 8 * C && exact_fit) &&
+                               (wgs <= 512 || rem == 0 || (rem >= 440 && wgs > 1024) || P >= C);
         // 16-row items with one staging buffer, two workgroups per CU (four
         // waves per SIMD instead of the two of a 16-row workgroup alone), where
         // they fill the 512 slots in one round: C = 961..1024 (+4-9% over the
-        // paired two-stage 16-row items at P = 0..4096; -2% at P = 16384)
-        const bool one_stage16 = !paged && C > 960 && C <= 1024 && P <= 4 * C;
+        // paired two-stage 16-row items at P = 0..4096; -2% at P = 16384), and
+        // C = 880..960 with P >= C (+2-6% over the 8-row one-stage items; at
+        // P = 0 the two-stage 16-row items there are 8% faster)
+        const bool one_stage16 = !paged && C >= 880 && C <= 1024 && P <= 4 * C && (C > 960 || P >= C);
         if (one_stage16) p = make_plan<T, 2, 4, 1>(C, kV_2x4s1, 0);
         else if (one_stage) p = make_plan<T, 1, 4, 1>(C, kV_1x4s1, 0);
         else if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired, paged);

@@ -195,24 +195,27 @@ def test_fp32_plans_balance_causal_work():
 def test_one_staging_buffer_only_where_its_items_fill_whole_rounds():
     """The one-stage shapes (64 KiB of K/V tiles and 1 KiB per Q row of LDS,
     two workgroups per CU: 512 slots) are planned for plain chunks: 8-row
-    items below 2048 rows with P <= 8C whose workgroups (one per 8 rows and
-    KV group) fill one round or whole rounds of the slots, or whose prefix
-    (P >= C) makes the items alike; 16-row items at C = 961..1024 with
-    P <= 4C; never for paged caches."""
+    items below 1800 rows whose workgroups (one per 8 rows and KV group) fill
+    one round, whole rounds or more than two rounds and most of a third of the
+    slots, or whose prefix (P >= C) makes the items alike, except past P = 8C
+    where 16- or 32-row items fill exactly 256 workgroups; 16-row items at
+    C = 961..1024 with P <= 4C, and at C = 880..960 with C <= P <= 4C; never
+    for paged caches."""
     ONE_STAGE, ONE_STAGE16 = 7, 8
     for C, P in [(512, 0), (1024 + 512, 0), (1530, 0), (1500, 100), (512, 128), (512, 129), (257, 0),
-                 (100, 0), (384, 1000), (768, 2000), (1536, 1536), (1100, 8800)]:
+                 (100, 0), (384, 1000), (768, 2000), (1536, 1536), (1100, 8800), (1100, 12000), (640, 10000),
+                 (1792, 1792)]:
         p = cpf.plan(C, P)
         assert p["variant"] == ONE_STAGE and p["lds_bytes"] == 65536 + 1024 * 8, (C, P, p)
         assert cpf.plan(C, P, paged=True)["variant"] != ONE_STAGE
-    for C, P in [(768, 0), (896, 0), (1024, 0), (512, 15872), (1024, 16000), (1100, 8801), (2048, 0),
-                 (2048, 2048), (1792, 1000)]:
+    for C, P in [(768, 0), (896, 0), (960, 0), (1024, 0), (512, 15872), (512, 8000), (1024, 16000), (2048, 0),
+                 (2048, 2048), (1792, 1000), (1900, 1900), (2000, 1000)]:
         assert cpf.plan(C, P)["variant"] != ONE_STAGE, (C, P)
-    for C, P in [(961, 0), (1000, 13), (1024, 0), (1024, 4096)]:
+    for C, P in [(880, 880), (896, 896), (960, 3840), (961, 0), (1000, 13), (1024, 0), (1024, 4096)]:
         p = cpf.plan(C, P)
         assert p["variant"] == ONE_STAGE16 and p["lds_bytes"] == 65536 + 1024 * 16 and p["grid"] <= 512, (C, P, p)
         assert cpf.plan(C, P, paged=True)["variant"] != ONE_STAGE16
-    for C, P in [(960, 0), (1025, 0), (1024, 4097), (768, 0)]:
+    for C, P in [(879, 879), (880, 0), (960, 959), (1025, 0), (1024, 4097), (768, 0)]:
         assert cpf.plan(C, P)["variant"] != ONE_STAGE16, (C, P)
 
 
