@@ -1533,8 +1533,17 @@ Plan choose_plan(int C, int P, bool paged) {
         // C = 880..960 with P >= C (+2-6% over the 8-row one-stage items; at
         // P = 0 the two-stage 16-row items there are 8% faster)
         const bool one_stage16 = !paged && C >= 880 && C <= 1024 && P <= 4 * C && (C > 960 || P >= C);
+        // The same 16-row items, unpaired over several rounds of the 512
+        // slots, heaviest first: for causal chunks of 1100..1599 rows (T=1400
+        // +10%, T=1200 +4%) and from 2048 rows wherever the 32-row items would
+        // run unpaired, i.e. could not pair into one round of 256 workgroups
+        // (C=2560 P=1000 +12%, C=2100 P=12000 +13%, T=2300 +5%).
+        const bool c32_unpaired = c32.t <= c16.t && c32.t <= c8.t && !c32.paired;
+        const bool one_stage16u = !paged && !one_stage16 && !one_stage &&
+                                  ((C >= 1100 && C < 1600 && P < C) || (C >= 2048 && c32_unpaired));
         if (one_stage16) p = make_plan<T, 2, 4, 1>(C, kV_2x4s1, 0);
         else if (one_stage) p = make_plan<T, 1, 4, 1>(C, kV_1x4s1, 0);
+        else if (one_stage16u) p = make_plan<T, 2, 4, 1>(C, kV_2x4s1, 0);
         else if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired, paged);
         else if (c16.t <= c8.t) p = make_plan<T, 2, 4>(C, kV_2x4, c16.paired, paged);
         else p = make_plan<T, 1, 4>(C, kV_1x4, c8.paired, paged);

@@ -183,10 +183,11 @@ def test_fp32_plans_balance_causal_work():
     estimate): (rows per item, workgroups, items per workgroup)."""
     want = {(2048, 2048): (32, 256, 2), (2048, 0): (32, 256, 2), (512, 15872): (16, 256, 1),
             (1024, 0): (16, 512, 1), (1536, 0): (8, 1536, 1), (512, 0): (8, 512, 1), (600, 0): (16, 304, 1),
-            (255, 3): (8, 256, 1), (1000, 13): (16, 504, 1), (1500, 100): (8, 1504, 1), (2049, 7): (32, 520, 1),
+            (255, 3): (8, 256, 1), (1000, 13): (16, 504, 1), (1500, 100): (8, 1504, 1), (2049, 7): (16, 1032, 1),
             (1024, 16384): (32, 256, 1), (1100, 0): (16, 552, 1),
             (17, 31): (8, 24, 1), (768, 0): (16, 384, 1), (1530, 0): (8, 1536, 1), (768, 2000): (8, 768, 1),
-            (1100, 4400): (8, 1104, 1), (300, 3000): (8, 304, 1)}
+            (1100, 4400): (8, 1104, 1), (300, 3000): (8, 304, 1), (1400, 0): (16, 704, 1),
+            (2560, 1000): (16, 1280, 1), (4096, 0): (32, 512, 2)}
     for (C, P), w in want.items():
         p = cpf.plan(C, P)
         assert (p["rows_per_item"], p["grid"], p["items_per_workgroup"]) == w, (C, P, p)
