@@ -1491,10 +1491,11 @@ inline ShapeCost shape_cost(int C, int P, int H, double eff, double item) {
 // fp32 (contiguous or paged): 32, 16 or 8 rows x 4 heads per work item (16-,
 // 8- or 4-wave workgroups, 4 key-split waves over 128-key tiles), paired or
 // not, whichever the estimate above makes fastest (relative efficiencies 1,
-// 0.92, 0.68, measured on balanced grids).  Long chunks take 32 rows in pairs;
-// a short prompt (P small against C) takes smaller items so that causal work
-// evens out over the CUs (C=1024 at P=0: 1.5x the throughput of unpaired
-// 32-row items).  bf16: 64-key tiles over 2 waves, 64 rows per work item (16
+// 0.92, 0.68, measured on balanced grids), unless one of the one-stage rules
+// below applies (plain caches: 8- or 16-row items with one staging buffer, two
+// workgroups per CU, where measured plan sweeps put them ahead).  Long chunks
+// take 32 rows in pairs; a short prompt (P small against C) takes smaller
+// items so that causal work evens out over the CUs.  bf16: 64-key tiles over 2 waves, 64 rows per work item (16
 // waves) from 4096 rows on, where row tiles still pair into 256 workgroups
 // (each staged tile then serves twice the queries: ~3% faster on long
 // prefixes, whose K/V exceed the L2), 32 rows (8-wave workgroups, two per CU)
