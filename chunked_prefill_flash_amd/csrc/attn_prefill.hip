@@ -282,7 +282,7 @@ __global__ void __launch_bounds__(64 * NW * KS, ST == 1 ? NW * KS / 2 : 1)
 attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
                     float* __restrict__ out, int C, int P, int n_row_tiles, int paired, PagedCache pg,
                     KeySplit ks, unsigned long long* __restrict__ clk) {
-    static_assert(ST == 2 || (ST == 1 && MODE == 0), "one staging buffer: plain contiguous caches only");
+    static_assert(ST == 2 || (ST == 1 && (MODE & kSplit) == 0), "one staging buffer: no key splits");
     // Clock log (attn_prefill_clocked; null otherwise): thread 0 stores, with
     // ordinary vector stores, the shader-clock counter and the fixed 100 MHz
     // counter at the workgroup's start and end, and the shader clock at the
@@ -791,10 +791,20 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         };
         // One staging buffer: every tile is consumed, then the next is loaded
         // into the same buffer; the other workgroup on the CU computes meanwhile.
+        // Paged: the table entries of tile t+2 are read while tile t is
+        // consumed and their offsets stored before the barrier that ends it,
+        // into the slot tile t's loads used.
         if constexpr (ST == 1) {
             for (int t = 0; t < ntiles; ++t) {
                 const VOps vo = prefetch_v(std::integral_constant<int, 0>{}, t);
+                int ent = 0;
+                if constexpr (PAGED) {
+                    if (t + 2 < ntiles) ent = fetch_entry(t + 2);
+                }
                 consume(std::integral_constant<int, 0>{}, t, vo);
+                if constexpr (PAGED) {
+                    if (t + 2 < ntiles) store_offset(t + 2, ent);
+                }
                 __syncthreads();                      // every wave is done with the tile
                 if (t + 1 < ntiles) {
                     issue_tile(t + 1, 0);
@@ -1521,19 +1531,23 @@ Plan choose_plan(int C, int P, bool paged) {
         // causal items (T=768 -11%), near 2048 rows to the 32-row items (C=1900
         // to 2000: -4 to -7%) and on prefixes past 8C where 16- or 32-row
         // items fill exactly the 256 CUs (C=512 P=15872 -3%, C=1024 P=16000
-        // -4%).  Plain caches only.
+        // -4%).  Paged caches take it in one round only (C=512 P=0 and C=384
+        // P=1000 20% faster, but 5-13% slower over more rounds, where each
+        // tile's row offsets sit on its critical path); the 16-row one-stage
+        // plans below have no LDS left for the offsets and stay plain.
         const int wgs = 8 * ((C + 7) / 8);
         const int rem = wgs % 512;
         const bool exact_fit = 8 * ((C + 31) / 32) == 256 || 8 * ((C + 15) / 16) == 256;
-        const bool one_stage = !paged && C < 1800 && !(P > 8 * C && exact_fit) &&
-                               (wgs <= 512 || rem == 0 || (rem >= 440 && wgs > 1024) || P >= C);
+        const bool os16_shape = C >= 880 && C <= 1024 && P <= 4 * C && (C > 960 || P >= C);
+        const bool one_stage = !os16_shape && C < 1800 && !(P > 8 * C && exact_fit) &&
+                               (wgs <= 512 || (!paged && (rem == 0 || (rem >= 440 && wgs > 1024) || P >= C)));
         // 16-row items with one staging buffer, two workgroups per CU (four
         // waves per SIMD instead of the two of a 16-row workgroup alone), where
         // they fill the 512 slots in one round: C = 961..1024 (+4-9% over the
         // paired two-stage 16-row items at P = 0..4096; -2% at P = 16384), and
         // C = 880..960 with P >= C (+2-6% over the 8-row one-stage items; at
         // P = 0 the two-stage 16-row items there are 8% faster)
-        const bool one_stage16 = !paged && C >= 880 && C <= 1024 && P <= 4 * C && (C > 960 || P >= C);
+        const bool one_stage16 = !paged && os16_shape;   // paged: the two-stage plans
         // The same 16-row items, unpaired over several rounds of the 512
         // slots, heaviest first: for causal chunks of 1100..1599 rows (T=1400
         // +10%, T=1200 +4%) and from 2048 rows wherever the 32-row items would
@@ -1543,7 +1557,7 @@ Plan choose_plan(int C, int P, bool paged) {
         const bool one_stage16u = !paged && !one_stage16 && !one_stage &&
                                   ((C >= 1100 && C < 1600 && P < C) || (C >= 2048 && c32_unpaired));
         if (one_stage16) p = make_plan<T, 2, 4, 1>(C, kV_2x4s1, 0);
-        else if (one_stage) p = make_plan<T, 1, 4, 1>(C, kV_1x4s1, 0);
+        else if (one_stage) p = make_plan<T, 1, 4, 1>(C, kV_1x4s1, 0, paged);
         else if (one_stage16u) p = make_plan<T, 2, 4, 1>(C, kV_2x4s1, 0);
         else if (c32.t <= c16.t && c32.t <= c8.t) p = make_plan<T, 4, 4>(C, kV_4x4, c32.paired, paged);
         else if (c16.t <= c8.t) p = make_plan<T, 2, 4>(C, kV_2x4, c16.paired, paged);
@@ -1593,8 +1607,8 @@ hipError_t dispatch(const Plan& p, const void* q, const void* k, const void* v, 
             if constexpr ((MODE & kSplit) != 0) return hipErrorInvalidValue;   // never planned
             else return launch<T, 4, 2, MODE>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
         case kV_2x4: return launch<T, 2, 4, MODE>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
-        case kV_1x4s1:   // planned for fp32 plain caches only
-            if constexpr (MODE != kPlain || sizeof(T) != 4) return hipErrorInvalidValue;
+        case kV_1x4s1:   // planned for fp32 only, never with key splits
+            if constexpr ((MODE & kSplit) != 0 || sizeof(T) != 4) return hipErrorInvalidValue;
             else return launch<T, 1, 4, MODE, 1>(p, q, k, v, out, C, P, pg, ksp, clk, stream);
         case kV_2x4s1:   // planned for fp32 plain caches only
             if constexpr (MODE != kPlain || sizeof(T) != 4) return hipErrorInvalidValue;

@@ -199,16 +199,21 @@ def test_one_staging_buffer_only_where_its_items_fill_whole_rounds():
     items below 1800 rows whose workgroups (one per 8 rows and KV group) fill
     one round, whole rounds or more than two rounds and most of a third of the
     slots, or whose prefix (P >= C) makes the items alike, except past P = 8C
-    where 16- or 32-row items fill exactly 256 workgroups; 16-row items at
-    C = 961..1024 with P <= 4C, and at C = 880..960 with C <= P <= 4C; never
-    for paged caches."""
+    where 16- or 32-row items fill exactly 256 workgroups (paged caches: one
+    round only, with the row offsets of two tiles in LDS); 16-row items at
+    C = 961..1024 with P <= 4C, and at C = 880..960 with C <= P <= 4C (plain
+    caches only)."""
     ONE_STAGE, ONE_STAGE16 = 7, 8
     for C, P in [(512, 0), (1024 + 512, 0), (1530, 0), (1500, 100), (512, 128), (512, 129), (257, 0),
                  (100, 0), (384, 1000), (768, 2000), (1536, 1536), (1100, 8800), (1100, 12000), (640, 10000),
                  (1792, 1792)]:
         p = cpf.plan(C, P)
         assert p["variant"] == ONE_STAGE and p["lds_bytes"] == 65536 + 1024 * 8, (C, P, p)
-        assert cpf.plan(C, P, paged=True)["variant"] != ONE_STAGE
+        pp = cpf.plan(C, P, paged=True)                   # paged: one round of the slots only
+        if p["grid"] <= 512:
+            assert pp["variant"] == ONE_STAGE and pp["lds_bytes"] == 65536 + 1024 * 8 + 2 * 4 * 128, (C, P, pp)
+        else:
+            assert pp["variant"] != ONE_STAGE, (C, P, pp)
     for C, P in [(768, 0), (896, 0), (960, 0), (1024, 0), (512, 15872), (512, 8000), (1024, 16000), (2048, 0),
                  (2048, 2048), (1792, 1000), (1900, 1900), (2000, 1000)]:
         assert cpf.plan(C, P)["variant"] != ONE_STAGE, (C, P)
