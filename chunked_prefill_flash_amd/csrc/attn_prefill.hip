@@ -1567,9 +1567,14 @@ Plan choose_plan(int C, int P, bool paged) {
         // 256 workgroups would leave half the slots empty: they stay unpaired
         // (C=2048 P=2048: 69.1 -> 62.5 us, P=500: 39.8 -> 36.9 us against
         // paired (4,2) items, with the heavy/light placement below)
-        p = C >= 2048 ? (C >= 4096 ? make_plan<T, 8, 2>(C, kV_8x2, shape_cost(C, P, 64, 1.0, 64.0 * 177.0).paired,
-                                                            paged)
-                                             : make_plan<T, 4, 2>(C, kV_4x2, 0, paged))
+        // 32-row items also for 1025..2047 rows against long prefixes, where
+        // 16-row ones would take more than one round of 512 workgroups (C=1100
+        // P=12000 6%, C=1536 P=1536 4%, C=1800 P=3000 8%, C=2000 P=2000 8%
+        // faster; at C=1100..1200 P=C and at P=0 the 16-row items stay 11-13%
+        // ahead)
+        p = C >= 2048 || (C > 1024 && (P >= 4 * C || (C >= 1400 && P >= C)))
+                ? (C >= 4096 ? make_plan<T, 8, 2>(C, kV_8x2, shape_cost(C, P, 64, 1.0, 64.0 * 177.0).paired, paged)
+                             : make_plan<T, 4, 2>(C, kV_4x2, 0, paged))
             : C >= 256 ? make_plan<T, 2, 4>(C, kV_2x4, 0, paged)
                        : make_plan<T, 1, 4>(C, kV_1x4, -1, paged);
     }
