@@ -201,12 +201,13 @@ def test_every_launch_variant(C, P):
     full_check("plain", C, P, "f32")
 
 
-@pytest.mark.parametrize("C,P", [(300, 1000), (1100, 50), (1024, 16), (4100, 10)])
+@pytest.mark.parametrize("C,P", [(300, 1000), (1100, 50), (1024, 16), (1500, 1500), (4100, 10)])
 def test_bf16_full_compare(C, P):
     """bf16 through the 16-row, 32-row and 64-row work items (the last with a
     ragged final row tile); the 16-row ones both in the heavy/light order of
     one round of two workgroups per CU (300 and 1024 rows) and heaviest first
-    over more rounds (1100 rows)."""
+    over more rounds (1100 rows); the 32-row ones heavy/light (1500 rows
+    against a prefix of as many)."""
     full_check("plain", C, P, "bf16")
 
 
