@@ -32,7 +32,10 @@
 // * K/V tiles go from HBM straight into LDS (bounds-checked buffer loads with
 //   an LDS destination), rows unpadded with their 16-byte chunks XOR-permuted
 //   per row so the MFMA operand reads avoid bank conflicts; the next tile's
-//   loads are in flight while the current tile is consumed (two stages).
+//   loads are in flight while the current tile is consumed (two stages), or,
+//   in the one-stage plans for short and mid-size chunks, two workgroups share
+//   a CU and one computes while the other's loads land.  fp32 Q rows take the
+//   same path into LDS, once per work item for all its waves.
 // * A workgroup is NW row-waves x KS key-split waves.  Key-split waves take
 //   alternate 32-key sub-blocks of each tile and are merged once at the end
 //   with the log-sum-exp rule ("FlashAttention and inference kernels",
