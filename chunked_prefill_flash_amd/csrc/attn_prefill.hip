@@ -795,8 +795,9 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
         // One staging buffer: every tile is consumed, then the next is loaded
         // into the same buffer; the other workgroup on the CU computes meanwhile.
         // Paged: the table entries of tile t+2 are read while tile t is
-        // consumed and their offsets stored before the barrier that ends it,
-        // into the slot tile t's loads used.
+        // consumed and their offsets stored while tile t+1's loads are in
+        // flight, into the slot tile t's loads used (read before the barrier
+        // that ends tile t); the barrier after those loads publishes them.
         if constexpr (ST == 1) {
             for (int t = 0; t < ntiles; ++t) {
                 const VOps vo = prefetch_v(std::integral_constant<int, 0>{}, t);
@@ -805,12 +806,12 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     if (t + 2 < ntiles) ent = fetch_entry(t + 2);
                 }
                 consume(std::integral_constant<int, 0>{}, t, vo);
-                if constexpr (PAGED) {
-                    if (t + 2 < ntiles) store_offset(t + 2, ent);
-                }
                 __syncthreads();                      // every wave is done with the tile
                 if (t + 1 < ntiles) {
                     issue_tile(t + 1, 0);
+                    if constexpr (PAGED) {
+                        if (t + 2 < ntiles) store_offset(t + 2, ent);
+                    }
                     stage_next_q(t);
                     __builtin_amdgcn_s_waitcnt(0x3f70);
                     __syncthreads();
@@ -1534,16 +1535,19 @@ Plan choose_plan(int C, int P, bool paged) {
         // causal items (T=768 -11%), near 2048 rows to the 32-row items (C=1900
         // to 2000: -4 to -7%) and on prefixes past 8C where 16- or 32-row
         // items fill exactly the 256 CUs (C=512 P=15872 -3%, C=1024 P=16000
-        // -4%).  Paged caches take it in one round only (C=512 P=0 and C=384
-        // P=1000 20% faster, but 5-13% slower over more rounds, where each
-        // tile's row offsets sit on its critical path); the 16-row one-stage
-        // plans below have no LDS left for the offsets and stay plain.
+        // -4%).  Paged caches take it in one round (C=512 P=0 and C=384 P=1000
+        // 20% faster) and over more rounds only from 1025 rows against
+        // prefixes of 8C (C=1100 P=8800 16%, C=1536 P=12288 6% faster; 3-11%
+        // slower at C=768 P=2000..12000 and C=1536 P=1536, where each tile's
+        // row offsets weigh more); the 16-row one-stage plans below have no
+        // LDS left for the offsets and stay plain.
         const int wgs = 8 * ((C + 7) / 8);
         const int rem = wgs % 512;
         const bool exact_fit = 8 * ((C + 31) / 32) == 256 || 8 * ((C + 15) / 16) == 256;
         const bool os16_shape = C >= 880 && C <= 1024 && P <= 4 * C && (C > 960 || P >= C);
         const bool one_stage = !os16_shape && C < 1800 && !(P > 8 * C && exact_fit) &&
-                               (wgs <= 512 || (!paged && (rem == 0 || (rem >= 440 && wgs > 1024) || P >= C)));
+                               (wgs <= 512 || (paged ? C > 1024 && P >= 8 * C
+                                                     : rem == 0 || (rem >= 440 && wgs > 1024) || P >= C));
         // 16-row items with one staging buffer, two workgroups per CU (four
         // waves per SIMD instead of the two of a 16-row workgroup alone), where
         // they fill the 512 slots in one round: C = 961..1024 (+4-9% over the

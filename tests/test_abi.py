@@ -199,8 +199,9 @@ def test_one_staging_buffer_only_where_its_items_fill_whole_rounds():
     items below 1800 rows whose workgroups (one per 8 rows and KV group) fill
     one round, whole rounds or more than two rounds and most of a third of the
     slots, or whose prefix (P >= C) makes the items alike, except past P = 8C
-    where 16- or 32-row items fill exactly 256 workgroups (paged caches: one
-    round only, with the row offsets of two tiles in LDS); 16-row items at
+    where 16- or 32-row items fill exactly 256 workgroups (paged caches, with
+    the row offsets of two tiles in LDS: one round, or more rounds from 1025
+    rows against prefixes of 8C); 16-row items at
     C = 961..1024 with P <= 4C, and at C = 880..960 with C <= P <= 4C (plain
     caches only)."""
     ONE_STAGE, ONE_STAGE16 = 7, 8
@@ -209,8 +210,8 @@ def test_one_staging_buffer_only_where_its_items_fill_whole_rounds():
                  (1792, 1792)]:
         p = cpf.plan(C, P)
         assert p["variant"] == ONE_STAGE and p["lds_bytes"] == 65536 + 1024 * 8, (C, P, p)
-        pp = cpf.plan(C, P, paged=True)                   # paged: one round of the slots only
-        if p["grid"] <= 512:
+        pp = cpf.plan(C, P, paged=True)   # paged: one round, or more from 1025 rows against P >= 8C
+        if p["grid"] <= 512 or (C > 1024 and P >= 8 * C):
             assert pp["variant"] == ONE_STAGE and pp["lds_bytes"] == 65536 + 1024 * 8 + 2 * 4 * 128, (C, P, pp)
         else:
             assert pp["variant"] != ONE_STAGE, (C, P, pp)

@@ -86,11 +86,13 @@ def test_paged_full_size_c2048_p2048():
 
 
 @pytest.mark.parametrize("C,P,dtype", [(600, 200, "f32"), (1800, 900, "f32"), (384, 1000, "f32"), (512, 0, "f32"),
+                                     (1100, 8800, "f32"),
                                      (2048, 500, "bf16"), (4096, 300, "bf16")])
 def test_paged_equals_contiguous_bitwise(C, P, dtype):
     """Same launch plan, same arithmetic: the paged path must reproduce the
     contiguous path bit for bit (fp32 16-row and 32-row work items with two
-    staging buffers and 8-row ones with one in the heavy/light order;
+    staging buffers and 8-row ones with one, in the heavy/light order and
+    heaviest first;
     bf16 32-row and 64-row ones)."""
     q, k, v = synth.case_plain(C, P, 5400 + C)
     kp, vp, table = synth.to_pages(k, v, 16, 5401 + C)
