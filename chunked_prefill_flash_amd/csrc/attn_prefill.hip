@@ -1748,12 +1748,19 @@ attn_status_t launch_splitkv(const Plan& p, const void* q, const void* kCache, c
 
 }  // namespace
 
+// Chunk and cache sizes the launch arithmetic is planned for: row, tile and
+// grid counts and the planner's comparisons stay within int.  The output
+// alone of a chunk past kMaxChunkRows (8 KiB per row) would exceed a GPU's
+// memory.
+constexpr int kMaxChunkRows = 1 << 26;
+static bool sizes_ok(int C, int P) { return C >= 0 && C <= kMaxChunkRows && P >= 0 && P <= INT_MAX - C; }
+
 extern "C" {
 
 attn_status_t attn_prefill_validate(const void* q, const void* kCache, const void* vCache, const float* out,
                                     int C, int P, attn_dtype_t dtype) {
     if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
-    if (C < 0 || P < 0 || P > INT_MAX - C) return ATTN_ERR_INVALID_ARG;
+    if (!sizes_ok(C, P)) return ATTN_ERR_INVALID_ARG;
     if (C == 0) return ATTN_OK;
     if (!q || !kCache || !vCache || !out) return ATTN_ERR_NULL_PTR;
     const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kCache) |
@@ -1771,7 +1778,7 @@ attn_status_t attn_prefill_validate(const void* q, const void* kCache, const voi
 attn_status_t attn_prefill_plan(int C, int P, attn_dtype_t dtype, int paged, int* plan) {
     if (!plan) return ATTN_ERR_NULL_PTR;
     if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
-    if (C < 0 || P < 0 || P > INT_MAX - C) return ATTN_ERR_INVALID_ARG;
+    if (!sizes_ok(C, P)) return ATTN_ERR_INVALID_ARG;
     const Plan p = plan_for(C > 0 ? C : 1, P, dtype, paged != 0);
     plan[0] = p.rows;
     plan[1] = p.ks;
@@ -1822,7 +1829,7 @@ attn_status_t attn_prefill_clocked(const void* q, const void* kCache, const void
 attn_status_t attn_prefill_splitkv_workspace(int C, int P, attn_dtype_t dtype, size_t* bytes, int* splits) {
     if (!bytes) return ATTN_ERR_NULL_PTR;
     if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
-    if (C < 0 || P < 0 || P > INT_MAX - C) return ATTN_ERR_INVALID_ARG;
+    if (!sizes_ok(C, P)) return ATTN_ERR_INVALID_ARG;
     if (C == 0) {
         *bytes = 0;
         if (splits) *splits = 0;
@@ -1938,7 +1945,7 @@ attn_status_t attn_prefill_paged_validate(const void* q, const void* kPages, con
                                           const int* blockTable, int numBlocks, int pageSize, const float* out,
                                           int C, int P, attn_dtype_t dtype) {
     if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
-    if (C < 0 || P < 0 || P > INT_MAX - C || pageSize <= 0 || numBlocks <= 0) return ATTN_ERR_INVALID_ARG;
+    if (!sizes_ok(C, P) || pageSize <= 0 || numBlocks <= 0) return ATTN_ERR_INVALID_ARG;
     const size_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
     const size_t pool = (size_t)numBlocks * (size_t)pageSize * kHKV * kD * esz;
     if (pool > 0xFFFFFFFFull) return ATTN_ERR_INVALID_ARG;     // page pool addressed with 32-bit offsets
