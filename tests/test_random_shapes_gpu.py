@@ -96,16 +96,20 @@ def test_wide_sweep_sampled_rows():
     1-256 positions), split-KV, paged split-KV, split-KV without a workspace
     and per-row; C log-uniform in [1, 2500], P in [0, 6000] (0 one time in
     five).  CPF_SWEEP_CASES sets the number of cases (default 200, a few
-    seconds; 3000 take under two minutes)."""
+    seconds; 3000 take under two minutes), CPF_SWEEP_MAX_C and CPF_SWEEP_MAX_P
+    the ranges' upper ends (the planner's multi-round rules for 1025+ rows
+    against prefixes of 8C need a wider P)."""
     n = int(os.environ.get("CPF_SWEEP_CASES", "200"))
+    max_c = int(os.environ.get("CPF_SWEEP_MAX_C", "2500"))
+    max_p = int(os.environ.get("CPF_SWEEP_MAX_P", "6000"))
     r = synth.uniform53(778, 8 * n)
     bad = []
     for t in range(n):
         u = r[8 * t: 8 * t + 8]
         entry = ("prefill", "paged", "splitkv", "rowwise", "paged_splitkv", "noalloc")[int(u[0] * 6) % 6]
         dtype = "bf16" if u[1] < 0.5 else "f32"
-        C = max(1, int(round(math.exp(u[2] * math.log(2500)))))
-        P = 0 if u[3] < 0.2 else int(round(math.exp(u[4] * math.log(6000))))
+        C = max(1, int(round(math.exp(u[2] * math.log(max_c)))))
+        P = 0 if u[3] < 0.2 else int(round(math.exp(u[4] * math.log(max_p))))
         page = (1, 2, 7, 16, 31, 64, 100, 128, 256)[int(u[5] * 9) % 9]
         if entry == "rowwise" and C * (P + C) > 3e6:
             entry = "prefill"   # the per-row baseline is slow on big shapes
@@ -150,4 +154,6 @@ def test_wide_sweep_sampled_rows():
         ok = ok and all(bool(np.all(got[p - P, 0] == 4.0)) for p in plants)
         if not ok:
             bad.append((t, entry, dtype, C, P, page))
+        if (t + 1) % 50 == 0:   # progress for long sweeps (visible with -s)
+            print("sweep: %d of %d cases, %d failed" % (t + 1, n, len(bad)), flush=True)
     assert not bad, "%d of %d cases failed, first %s" % (len(bad), n, bad[:5])
