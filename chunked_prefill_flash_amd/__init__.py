@@ -228,9 +228,14 @@ def attn_prefill_clocked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out:
     a contiguous int64 device tensor of at least that many rows, written in
     place with nothing allocated or cleared (a mark not written keeps its old
     value), so that a timed loop can log one of its calls."""
+    if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype in %s" % list(DTYPES))
     C = q.shape[0]
     if P is None:
         P = k.shape[0] - C
+    if q.dim() != 3 or q.shape[1:] != (HQ, D) or k.shape != (P + C, HKV, D) or v.shape != k.shape:
+        raise ValueError("bad shapes q %s k %s v %s for P=%d" % (tuple(q.shape), tuple(k.shape), tuple(v.shape), P))
+    _gpu_tensors(q.device, q=q, k=k, v=v)
     grid = plan(C, P, q.dtype)["grid"] if C > 0 else 0
     s = _stream(stream, q.device)
     if clocks is None:
@@ -239,11 +244,6 @@ def attn_prefill_clocked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out:
     elif (clocks.dtype != torch.int64 or clocks.device != q.device or not clocks.is_contiguous()
           or clocks.dim() != 2 or clocks.shape[1] != CLOCK_WORDS or clocks.shape[0] < grid):
         raise ValueError("clocks must be a contiguous int64 [>= %d][%d] tensor on %s" % (grid, CLOCK_WORDS, q.device))
-    if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype in %s" % list(DTYPES))
-    if q.dim() != 3 or q.shape[1:] != (HQ, D) or k.shape != (P + C, HKV, D) or v.shape != k.shape:
-        raise ValueError("bad shapes q %s k %s v %s for P=%d" % (tuple(q.shape), tuple(k.shape), tuple(v.shape), P))
-    _gpu_tensors(q.device, q=q, k=k, v=v)
     out = _out_tensor(out, C, q.device, s)
     with torch.cuda.device(q.device):
         st = load_library().attn_prefill_clocked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), C, P,
@@ -271,6 +271,8 @@ def _paged_args(q, k_pages, v_pages, block_table, P):
                          % (tuple(k_pages.shape), tuple(v_pages.shape)))
     C = q.shape[0]
     num_blocks, page_size = k_pages.shape[0], k_pages.shape[1]
+    if num_blocks < 1 or page_size < 1:
+        raise ValueError("pages must hold at least one page of at least one position, got %s" % (tuple(k_pages.shape),))
     if block_table.dtype != torch.int32 or block_table.dim() != 1 or \
             block_table.shape[0] < -(-(P + C) // page_size):
         raise ValueError("block_table must be int32 with at least ceil((P+C)/pageSize) entries")

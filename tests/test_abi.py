@@ -381,3 +381,9 @@ def test_every_binding_rejects_host_tensors_and_bad_shapes():
         cpf.attn_naive(q, torch.zeros(3, 8, 64), torch.zeros(3, 8, 64))
     with pytest.raises(ValueError):
         cpf.attn_naive(q, torch.zeros(4, 8, 64), torch.zeros(4, 8, 64))
+    with pytest.raises(ValueError):   # pages of no positions
+        cpf.attn_prefill_paged(q, torch.zeros(2, 0, 8, 64), torch.zeros(2, 0, 8, 64), table, 2)
+    with pytest.raises(TypeError):    # dtype checked before the plan lookup
+        cpf.attn_prefill_clocked(q.double(), k.double(), k.double(), P=2)
+    with pytest.raises(ValueError):
+        cpf.attn_prefill_clocked(q, torch.zeros(4, 8, 64), torch.zeros(4, 8, 64), P=2)
