@@ -187,7 +187,7 @@ def test_fp32_plans_balance_causal_work():
             (1024, 16384): (32, 256, 1), (1100, 0): (16, 552, 1),
             (17, 31): (8, 24, 1), (768, 0): (16, 384, 1), (1530, 0): (8, 1536, 1), (768, 2000): (8, 768, 1),
             (1100, 4400): (8, 1104, 1), (300, 3000): (8, 304, 1), (1400, 0): (16, 704, 1),
-            (2560, 1000): (16, 1280, 1), (4096, 0): (32, 512, 2)}
+            (2560, 1000): (16, 1280, 1), (4096, 0): (32, 512, 2), (900, 1000): (16, 456, 1)}
     for (C, P), w in want.items():
         p = cpf.plan(C, P)
         assert (p["rows_per_item"], p["grid"], p["items_per_workgroup"]) == w, (C, P, p)

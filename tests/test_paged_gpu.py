@@ -64,6 +64,21 @@ def test_paged_fp32(page_size, C, P):
         assert np.all(got[p - P, 0] == np.float32(4.0))
 
 
+def test_paged_one_stage_over_several_rounds():
+    """The 8-row one-staging-buffer kernel over pages, in more rounds than
+    the 512 resident workgroups (1300 rows against a prefix of 10C), every
+    element against the oracle."""
+    C, P = 1300, 13000
+    assert cpf.plan(C, P, torch.float32, paged=True)["lds_bytes"] < 81920   # two workgroups per CU
+    q, k, v, plants = synth.case_planted_chunk(C, P, 5300, 3)
+    kp, vp, table = synth.to_pages(k, v, 16, 5301)
+    got = run_paged(q, kp, vp, table, P, "f32")
+    ref = oracle.attn_prefill_paged(q, kp, vp, table, P)
+    check(got, ref, "f32", what="paged C=%d P=%d page=16" % (C, P))
+    for p in plants:
+        assert np.all(got[p - P, 0] == np.float32(4.0))
+
+
 @pytest.mark.parametrize("page_size", [16, 33])
 def test_paged_bf16(page_size):
     C, P = 300, 1000

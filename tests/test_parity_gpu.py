@@ -191,13 +191,13 @@ def test_edge_grid(C, P, dtype):
 
 @pytest.mark.parametrize("C,P", [(255, 3), (256, 700), (300, 3000), (600, 0), (1000, 13), (1024, 1),
                                  (1500, 100), (2049, 7), (2100, 0), (2048, 500), (1530, 0), (512, 128),
-                                 (961, 2500), (1100, 0), (768, 2000)])
+                                 (961, 2500), (1100, 0), (768, 2000), (900, 1000), (2560, 1000)])
 def test_every_launch_variant(C, P):
     """Covers the fp32 work items of 8, 16 and 32 rows, paired and unpaired
     row tiles, one and two staging buffers (16-row items with one buffer at
-    C = 961..1024), the heavy/light and heaviest-first orders, an odd number
-    of tiles and ragged last tiles (the plan of each case is asserted in the
-    ABI tests)."""
+    C = 880..1024 in one round and from 1100 or 2048 rows over several), the
+    heavy/light and heaviest-first orders, an odd number of tiles and ragged
+    last tiles (the plan of each case is asserted in the ABI tests)."""
     full_check("plain", C, P, "f32")
 
 
