@@ -1647,9 +1647,8 @@ Plan split_plan(int C, int P, attn_dtype_t dtype) {
         // kernel below: with twice the keys per byte the FMA work is no longer
         // hidden behind the loads, and bf16 MFMAs are cheap enough.
         Plan p{};
-        const int total = P + 1;
-        int len = (total + 31) / 32;
-        len = max(64, (len + 63) / 64 * 64);
+        const long long total = (long long)P + 1;   // sums below in 64 bits: P may be near INT_MAX
+        const int len = (int)max(64LL, ((total + 31) / 32 + 63) / 64 * 64);
         p.rows = 1;
         p.ks = kDecWaves;
         p.threads = 64 * kDecWaves;
@@ -1659,7 +1658,7 @@ Plan split_plan(int C, int P, attn_dtype_t dtype) {
         p.n_row_tiles = 1;
         p.per_wg = 1;
         p.split_len = len;
-        p.splits = (total + len - 1) / len;
+        p.splits = (int)((total + len - 1) / len);
         p.grid = kHKV * p.splits;
         return p;
     }
@@ -1668,15 +1667,13 @@ Plan split_plan(int C, int P, attn_dtype_t dtype) {
                      : (dtype == ATTN_DTYPE_BF16 ? make_plan<__bf16, 2, 4>(C, kV_2x4) : make_plan<float, 2, 4>(C, kV_2x4));
     p.paired = 0;
     p.per_wg = 1;
-    const int total = P + C;
+    const long long total = (long long)P + C;   // sums below in 64 bits: P + C may be near INT_MAX
     const int base = p.n_row_tiles * kHKV;
     constexpr int kTargetWorkgroups = 256;
-    int s = (kTargetWorkgroups + base - 1) / base;
-    const int most = (total + 2 * p.bk - 1) / (2 * p.bk);
-    s = max(1, min(s, most));
-    int len = (total + s - 1) / s;
-    len = (len + p.bk - 1) / p.bk * p.bk;
-    p.splits = (total + len - 1) / len;
+    const long long most = (total + 2 * p.bk - 1) / (2 * p.bk);
+    const long long s = max(1LL, min((long long)(kTargetWorkgroups + base - 1) / base, most));
+    const long long len = ((total + s - 1) / s + p.bk - 1) / p.bk * p.bk;
+    p.splits = (int)((total + len - 1) / len);
     p.split_len = len;
     p.grid = base * p.splits;
     return p;
@@ -1748,12 +1745,16 @@ attn_status_t launch_splitkv(const Plan& p, const void* q, const void* kCache, c
 
 }  // namespace
 
-// Chunk and cache sizes the launch arithmetic is planned for: row, tile and
-// grid counts and the planner's comparisons stay within int.  The output
-// alone of a chunk past kMaxChunkRows (8 KiB per row) would exceed a GPU's
-// memory.
+// Chunk and cache sizes the launch arithmetic is planned for: row, tile, split
+// and grid counts, key offsets plus a split's length, and the planner's
+// comparisons stay within int.  The output alone of a chunk past
+// kMaxChunkRows (8 KiB per row), or the K/V of a cache past kMaxPositions (at
+// least 2 KiB per position), would exceed a GPU's memory.
 constexpr int kMaxChunkRows = 1 << 26;
-static bool sizes_ok(int C, int P) { return C >= 0 && C <= kMaxChunkRows && P >= 0 && P <= INT_MAX - C; }
+constexpr int kMaxPositions = 1 << 30;
+static bool sizes_ok(int C, int P) {
+    return C >= 0 && C <= kMaxChunkRows && P >= 0 && P <= kMaxPositions - C;
+}
 
 extern "C" {
 

@@ -55,15 +55,22 @@ extern "C" {
 #define ATTN_NUM_KV_HEADS 8
 #define ATTN_HEAD_DIM 64
 
-/* Element type of q, kCache and vCache.  out is always float32. */
-typedef enum {
+/* Element type of q, kCache and vCache.  out is always float32.  Any other
+ * value is rejected with ATTN_ERR_UNSUPPORTED_DTYPE; in C++ the enum takes int
+ * as its underlying type, so that such a value is still a representable
+ * attn_dtype_t when the library checks it. */
+typedef enum
+#ifdef __cplusplus
+    : int
+#endif
+{
     ATTN_DTYPE_F32 = 0,  /* IEEE binary32; scores and PV products in fp32 MFMA */
     ATTN_DTYPE_BF16 = 1  /* bfloat16; bf16 MFMA with fp32 accumulation, fp32 softmax state */
 } attn_dtype_t;
 
 typedef enum {
     ATTN_OK = 0,
-    ATTN_ERR_INVALID_ARG = 1,      /* C < 0, C > 2^26, P < 0, or P + C overflows int */
+    ATTN_ERR_INVALID_ARG = 1,      /* C < 0, C > 2^26, P < 0, or P + C > 2^30 */
     ATTN_ERR_NULL_PTR = 2,         /* a tensor pointer is NULL while C > 0 */
     ATTN_ERR_UNSUPPORTED_DTYPE = 3,/* dtype is not an attn_dtype_t value */
     ATTN_ERR_MISALIGNED = 4,       /* a tensor pointer is not 16-byte aligned */
@@ -82,7 +89,8 @@ typedef enum {
  *   out     device pointer, [C][32][64] float32, 16-byte aligned, written
  *   C       chunk length (number of query rows), 0 <= C <= 2^26 (67,108,864);
  *           C == 0 is a no-op
- *   P       prefix length already in the cache, P >= 0
+ *   P       prefix length already in the cache, 0 <= P <= 2^30 - C (no GPU's memory
+ *           holds a larger cache)
  *   dtype   element type of q, kCache, vCache
  *   stream  HIP stream to enqueue on (0 = the null stream)
  *

@@ -305,13 +305,13 @@ def test_plan_errors():
 
 
 def test_chunk_length_limit():
-    """Chunks up to 2^26 rows (more than any GPU's memory holds outputs for)
-    are planned with positive, exact grids in every mode; longer ones are
-    rejected before any launch arithmetic could overflow."""
+    """Chunks up to 2^26 rows and caches up to 2^30 positions (more than any
+    GPU's memory holds) are planned with positive, exact grids in every mode;
+    larger ones are rejected before any launch arithmetic could overflow."""
     big = 1 << 26
     for dt in (torch.float32, torch.bfloat16):
         for paged in (False, True):
-            for P in (0, 2 ** 31 - 1 - big):
+            for P in (0, 2 ** 30 - big):
                 p = cpf.plan(big, P, dt, paged)
                 items = (big + p["rows_per_item"] - 1) // p["rows_per_item"]
                 assert p["grid"] * p["items_per_workgroup"] >= items * 8 > 0
@@ -319,6 +319,8 @@ def test_chunk_length_limit():
                 cpf.plan(big + 1, 0, dt, paged)
             with pytest.raises(cpf.AttnError):
                 cpf.plan(2 ** 31 - 1, 0, dt, paged)
+            with pytest.raises(cpf.AttnError):
+                cpf.plan(big, 2 ** 30 - big + 1, dt, paged)
     far = dict(q=A, k=A + (1 << 40), vv=A + (2 << 40), out=A + (3 << 40))   # no overlap at 2^26 rows
     assert v(C=big, P=0, **far) == OK
     assert v(C=big + 1, P=0, **far) == INVALID
