@@ -937,6 +937,60 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* 
                     ml[1] = lt;
                 }
             }
+        } else if constexpr (KS > 1 && NW > 1) {
+            // Items of 16 rows or more: normalised rows through LDS, then
+            // full-line stores.  Wave (wr, 0) writes its 8 rows x 4 heads x 64
+            // dims into its own merge slots (read only by itself above), 16-byte
+            // chunks XOR-permuted by (row * 4 + head) % 16 so that a write
+            // instruction spreads over all banks; after a barrier every wave
+            // stores whole 1 KiB rows, four lanes per 64-byte line, as
+            // non-temporal writes.  (8-row items store from registers: there
+            // the extra barrier costs more than the whole lines gain.)
+            (void)ks;
+            (void)store_o;
+            float* const stg0 = reinterpret_cast<float*>(lds_raw);
+            constexpr int kSlotFloats = (KS - 1) * 34 * 64;       // one row-wave's merge slots
+            if (wp == 0 && wave_active) {
+                const float lt = half_sum(l);
+                const float inv = 1.0f / lt;
+                const int rw = (lane2 & 31) >> 2, hd = lane2 & 3;
+                const int f = (rw * 4 + hd) & 15;
+                float* const base = stg0 + wr * kSlotFloats + rw * 256 + hd * 64;
+                auto put = [&](int dim, f4 x) {   // dim: a multiple of 4
+                    const int c = dim >> 2;
+                    *reinterpret_cast<f4*>(base + ((c ^ f) << 2)) = x;
+                };
+                if constexpr (kF32) {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        put(8 * hh2 + 16 * a, f4{o0[4 * a] * inv, o1[4 * a] * inv, o0[4 * a + 1] * inv, o1[4 * a + 1] * inv});
+                        put(8 * hh2 + 16 * a + 4,
+                            f4{o0[4 * a + 2] * inv, o1[4 * a + 2] * inv, o0[4 * a + 3] * inv, o1[4 * a + 3] * inv});
+                    }
+                } else {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        put(4 * hh2 + 8 * a, f4{o0[4 * a] * inv, o0[4 * a + 1] * inv, o0[4 * a + 2] * inv, o0[4 * a + 3] * inv});
+                        put(4 * hh2 + 32 + 8 * a,
+                            f4{o1[4 * a] * inv, o1[4 * a + 1] * inv, o1[4 * a + 2] * inv, o1[4 * a + 3] * inv});
+                    }
+                }
+            }
+            __syncthreads();
+            const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(out + (size_t)i0 * kHQ * kD), (short)0, (uint32_t)item_rows * kHQ * kD * 4, 0x00020000);
+            int L = lane;
+            asm volatile("" : "+v"(L));
+            const int hd = L >> 4, c = L & 15;
+#pragma unroll
+            for (int u = 0; u < kRows / G::kWaves; ++u) {
+                const int r = wid + u * G::kWaves;               // item row; rows past the chunk are not written
+                const int rw = r & 7;
+                const float* src = stg0 + (r >> 3) * kSlotFloats + rw * 256 + hd * 64 + ((c ^ ((rw * 4 + hd) & 15)) << 2);
+                const f4 x = *reinterpret_cast<const f4*>(src);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ro,
+                                                       (uint32_t)((r * kHQ + g * kGroup) * kD * 4 + L * 16), 0, 2);
+            }
         } else if (wp == 0 && wave_active) {
             (void)ks;
             const float lt = half_sum(l);
