@@ -1126,28 +1126,31 @@ attn_merge_splits_kernel(const float* __restrict__ part, float* __restrict__ out
     const int ns = min(n, (P + row) / len + 1);
     const float* ml = part + (size_t)n * C * kHQ * kD;
     const size_t stride = (size_t)C * kHQ;              // between splits, in (row, head) units
-    // 64 splits at a time, all their loads issued together (indices clamped
-    // into range; the weight of a clamped slot is 0), combined online
+    // 32 splits at a time (the planners make at most 32), all their loads
+    // issued together (indices clamped into range; the weight of a clamped
+    // slot, and of lanes 32..63, is 0), combined online; the weighted sum of a
+    // chunk in four independent FMA chains
     float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 64) {
-        const int cnt = min(64, ns - s0);
-        const int sl = s0 + min(lane, cnt - 1);
+    for (int s0 = 0; s0 < ns; s0 += 32) {
+        const int cnt = min(32, ns - s0);
+        const int sl = s0 + min(lane & 31, cnt - 1);
         const float ms = ml[(sl * stride + qi) * 2];
         const float ls = ml[(sl * stride + qi) * 2 + 1];
         const float* src = part + ((size_t)s0 * stride + qi) * kD + lane;
-        float x[64];
+        float x[32];
 #pragma unroll
-        for (int t = 0; t < 64; ++t) x[t] = src[(size_t)min(t, cnt - 1) * stride * kD];
-        const float mc = wave_max64(lane < cnt ? ms : -INFINITY);
+        for (int t = 0; t < 32; ++t) x[t] = src[(size_t)min(t, cnt - 1) * stride * kD];
+        const bool valid = lane < cnt;                    // lanes 32..63 repeat 0..31
+        const float mc = wave_max64(valid ? ms : -INFINITY);
         const float mn = fmaxf(M, mc);                   // finite: every reached split saw a key
         const float scale = fast_exp2(M - mn);           // 0 on the first chunk
-        const float w = lane < cnt ? fast_exp2(ms - mn) : 0.f;
+        const float w = valid ? fast_exp2(ms - mn) : 0.f;
         L = L * scale + wave_sum64(w * ls);
-        float acc = 0.f;
+        float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 64; ++t)
-            acc = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), t)), x[t], acc);
-        O = O * scale + acc;
+        for (int t = 0; t < 32; ++t)
+            a[t & 3] = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), t)), x[t], a[t & 3]);
+        O = O * scale + ((a[0] + a[1]) + (a[2] + a[3]));
         M = mn;
     }
     out[(size_t)qi * kD + lane] = O / L;
