@@ -1804,10 +1804,11 @@ attn_status_t launch_splitkv(const Plan& p, const void* q, const void* kCache, c
 
 // Chunk and cache sizes the launch arithmetic is planned for: row, tile, split
 // and grid counts, key offsets plus a split's length, and the planner's
-// comparisons stay within int.  The output alone of a chunk past
-// kMaxChunkRows (8 KiB per row), or the K/V of a cache past kMaxPositions (at
+// comparisons stay within int (the merge kernel's (row, head) count
+// C * 32 among them).  The q and output rows of a chunk past kMaxChunkRows
+// (at least 12 KiB per row), or the K/V of a cache past kMaxPositions (at
 // least 2 KiB per position), would exceed a GPU's memory.
-constexpr int kMaxChunkRows = 1 << 26;
+constexpr int kMaxChunkRows = 1 << 25;
 constexpr int kMaxPositions = 1 << 30;
 static bool sizes_ok(int C, int P) {
     return C >= 0 && C <= kMaxChunkRows && P >= 0 && P <= kMaxPositions - C;

@@ -70,7 +70,7 @@ typedef enum
 
 typedef enum {
     ATTN_OK = 0,
-    ATTN_ERR_INVALID_ARG = 1,      /* C < 0, C > 2^26, P < 0, or P + C > 2^30 */
+    ATTN_ERR_INVALID_ARG = 1,      /* C < 0, C > 2^25, P < 0, or P + C > 2^30 */
     ATTN_ERR_NULL_PTR = 2,         /* a tensor pointer is NULL while C > 0 */
     ATTN_ERR_UNSUPPORTED_DTYPE = 3,/* dtype is not an attn_dtype_t value */
     ATTN_ERR_MISALIGNED = 4,       /* a tensor pointer is not 16-byte aligned */
@@ -87,7 +87,7 @@ typedef enum {
  *   kCache  device pointer, [P+C][8][64] of dtype, 16-byte aligned
  *   vCache  device pointer, [P+C][8][64] of dtype, 16-byte aligned
  *   out     device pointer, [C][32][64] float32, 16-byte aligned, written
- *   C       chunk length (number of query rows), 0 <= C <= 2^26 (67,108,864);
+ *   C       chunk length (number of query rows), 0 <= C <= 2^25 (33,554,432);
  *           C == 0 is a no-op
  *   P       prefix length already in the cache, 0 <= P <= 2^30 - C (no GPU's memory
  *           holds a larger cache)

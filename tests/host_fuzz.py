@@ -21,13 +21,13 @@ IMAX = 2 ** 31 - 1
 A = 0x10000000                       # fake, aligned, far-apart addresses: never dereferenced
 q, k, v, out, table = A, A + (1 << 40), A + (2 << 40), A + (3 << 40), A + (4 << 40)
 edges = [0, 1, 2, 7, 8, 31, 32, 63, 64, 127, 128, 255, 256, 879, 880, 960, 961, 1024, 1025, 1100, 1599, 1600,
-         1800, 2047, 2048, 4095, 4096, 2 ** 20, 2 ** 26 - 1, 2 ** 26, 2 ** 26 + 1, 2 ** 30 - 1, 2 ** 30, IMAX, -1,
+         1800, 2047, 2048, 4095, 4096, 2 ** 20, 2 ** 25 - 1, 2 ** 25, 2 ** 25 + 1, 2 ** 26, 2 ** 30 - 1, 2 ** 30, IMAX, -1,
          -IMAX - 1]
 rng = random.Random(7)
 chunks = edges + [int(2 ** rng.uniform(0, 31)) for _ in range(n_random)]
 calls = 0
 for C in chunks:
-    lim = (1 << 30) - C if 0 <= C <= (1 << 26) else 0
+    lim = (1 << 30) - C if 0 <= C <= (1 << 25) else 0
     prefixes = rng.sample(edges, 8) + [int(2 ** rng.uniform(0, 31)) for _ in range(4)]
     if lim > 0:
         prefixes += [lim, lim - 1, lim // 2, rng.randrange(lim)]

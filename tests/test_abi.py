@@ -305,10 +305,10 @@ def test_plan_errors():
 
 
 def test_chunk_length_limit():
-    """Chunks up to 2^26 rows and caches up to 2^30 positions (more than any
+    """Chunks up to 2^25 rows and caches up to 2^30 positions (more than any
     GPU's memory holds) are planned with positive, exact grids in every mode;
     larger ones are rejected before any launch arithmetic could overflow."""
-    big = 1 << 26
+    big = 1 << 25
     for dt in (torch.float32, torch.bfloat16):
         for paged in (False, True):
             for P in (0, 2 ** 30 - big):
@@ -321,7 +321,7 @@ def test_chunk_length_limit():
                 cpf.plan(2 ** 31 - 1, 0, dt, paged)
             with pytest.raises(cpf.AttnError):
                 cpf.plan(big, 2 ** 30 - big + 1, dt, paged)
-    far = dict(q=A, k=A + (1 << 40), vv=A + (2 << 40), out=A + (3 << 40))   # no overlap at 2^26 rows
+    far = dict(q=A, k=A + (1 << 40), vv=A + (2 << 40), out=A + (3 << 40))   # no overlap at 2^25 rows
     assert v(C=big, P=0, **far) == OK
     assert v(C=big + 1, P=0, **far) == INVALID
     nb, ns = cpf.splitkv_workspace(big, 1000)
